@@ -1,0 +1,149 @@
+/*
+ * pva.h — packed variable-length mixed-mask attention on MI355X (gfx950).
+ *
+ * The operation (forward only, inference):
+ *   Several sequences are packed back to back along one token axis, without
+ *   padding, and addressed by prefix sums of their lengths ("cu_seqlens").
+ *   This replaces the padded batch plus explicit (bsz, 1, seqlen, seqlen)
+ *   boolean mask described in "[RFC]: HunyuanImage 3.0 deployment",
+ *   Motivation (1), by the packed cu_seqlens layout of that RFC's Proposed
+ *   Change P0 ("Packed Attention for Multi-Request Batching").
+ *
+ *   Sequence s holds T_s text tokens followed by I_s image tokens,
+ *   L_s = T_s + I_s. Its mask is the RFC's Generalized Causal Attention
+ *   (Proposed Change P0, attention mask challenge; Model structure, item 1):
+ *   text row i (i < T_s) attends to keys 0..i; image rows attend to all L_s
+ *   keys of their sequence (the whole text prefix and every image token).
+ *   No row attends across sequences. For every sequence s and head h:
+ *       O = softmax(scale * Q K^T + mask) V,
+ *   accumulated in fp32, rows with no allowed key defined as zero (no such
+ *   row exists for L_s >= 1 under this mask).
+ *
+ * Layout: Q, K, V and O are [N, H, D] row-major (D contiguous), N = sum L_s,
+ * in pack order. All heads share one sequence structure (no GQA).
+ *
+ * Ownership: the caller owns every tensor and every stream. The library owns
+ * only a pva_seg_desc (host copy + device work list), freed by
+ * pva_seg_desc_free. No call allocates device memory except
+ * pva_seg_desc_build.
+ *
+ * Errors: every entry point returns a pva_status (0 on success). Arguments
+ * are validated on the host before any launch; nothing throws or aborts
+ * across this boundary. pva_last_error() returns a thread-local message
+ * for the last failing call on the calling thread. Kernel launches are
+ * asynchronous: faults surface at the caller's next synchronisation.
+ */
+#ifndef PVA_H_
+#define PVA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PVA_OK = 0,
+  PVA_ERR_INVALID_ARG = -1, /* a size, pointer, alignment or value is out of range   */
+  PVA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. D) */
+  PVA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed              */
+  PVA_ERR_NO_MEMORY = -4    /* host or device allocation failed                        */
+} pva_status;
+
+typedef enum { PVA_BF16 = 0, PVA_FP8_E4M3 = 1 } pva_dtype;
+
+/* Opaque, library-owned descriptor of one batch composition. */
+typedef struct pva_seg_desc pva_seg_desc;
+
+/*
+ * Segment-descriptor builder (host). From per-sequence (text_len, image_len)
+ * it derives cu_seqlens and, per query tile of BM rows and key tiles of BN
+ * keys, the tile classes of the mask above: key tiles below k_full_end are
+ * FULL (no masking), tiles from k_end on are SKIP (never visited), tiles in
+ * between are PARTIAL (masked element-wise). This is the block-sparse form of
+ * the mixed mask named in the RFC's attention mask challenge (Proposed Change
+ * P0). It then orders the (sequence, head, query-tile) work items for the
+ * varlen tile scheduler and uploads the work list to device memory with an
+ * asynchronous copy on `stream` (a hipStream_t; NULL = the null stream).
+ *
+ *   text_len, image_len : host int32 [nseq], copied; T >= 0, I >= 0, T+I >= 1
+ *   nseq                : >= 1, sum of lengths must fit in int32
+ *   num_heads           : H >= 1, H * head_dim * N must fit in int64
+ *   head_dim            : D in {64, 128}
+ *   dtype               : element type of Q/K/V the descriptor will serve
+ *   out                 : receives the descriptor on PVA_OK, NULL otherwise
+ * The host arrays are not referenced after return. The descriptor must
+ * outlive every launch that uses it (free only after those launches have
+ * completed on their streams).
+ */
+int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_t nseq,
+                       int32_t num_heads, int32_t head_dim, pva_dtype dtype, void* stream,
+                       pva_seg_desc** out);
+
+/* Same planning without touching any device: the result can be inspected
+ * (accessors below) but not launched. For host-side tests and tools. */
+int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, int32_t nseq,
+                            int32_t num_heads, int32_t head_dim, pva_dtype dtype,
+                            pva_seg_desc** out);
+
+/* Host view of the descriptor's cu_seqlens (int32 [nseq + 1]); valid until
+ * the descriptor is freed. */
+int pva_seg_desc_cu_seqlens(const pva_seg_desc* desc, const int32_t** host_cu, int32_t* len);
+
+/* Useful multiply-add FLOPs over allowed (query, key) pairs only:
+ * 4 * D * H * sum_s [T_s (T_s + 1) / 2 + I_s * L_s]. Returns -1 on NULL. */
+int64_t pva_seg_desc_useful_flops(const pva_seg_desc* desc);
+
+/* Tile shape the descriptor was planned with (query rows BM, keys BN). */
+int pva_seg_desc_tile(const pva_seg_desc* desc, int32_t* block_m, int32_t* block_n);
+
+/* Host view of the work list in launch order: int32 [n_items][8] records
+ * {seq, head, q0, q_rows, k_full_end, k_end, T, L}; seq = -1 marks an empty
+ * slot that keeps the XCD alignment of the list. Valid until freed. */
+int pva_seg_desc_work_items(const pva_seg_desc* desc, const int32_t** items, int32_t* n_items);
+
+/* Free a descriptor (NULL is a no-op). Releases its device work list with
+ * hipFree, which synchronises the device. */
+void pva_seg_desc_free(pva_seg_desc* desc);
+
+/*
+ * Packed mixed-mask attention forward, bf16 in, fp32 accumulate, bf16 out.
+ *
+ *   q, k, v    : device bf16 [N, H, D], 16-byte aligned
+ *   cu_seqlens : device int32 [nseq + 1] equal to the descriptor's
+ *   seg_desc   : built by pva_seg_desc_build with dtype PVA_BF16
+ *   scale      : softmax scale (finite, > 0), usually 1/sqrt(D)
+ *   out        : device bf16 [N, H, D], 16-byte aligned; every row of every
+ *                sequence is written; nothing outside [N, H, D] is touched
+ *   stream     : hipStream_t to launch on (NULL = null stream)
+ * Asynchronous; allocates nothing. With the environment variable PVA_CHECK=1
+ * the device cu_seqlens is copied back (synchronously) and compared with the
+ * descriptor's before the launch.
+ */
+int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                    const pva_seg_desc* seg_desc, float scale, void* out, void* stream);
+
+/*
+ * FP8 variant: q, k, v are OCP E4M3FN codes [N, H, D] (16-byte aligned) with
+ * one fp32 dequantisation scale per (sequence, head) and tensor
+ * (q_scale/k_scale/v_scale: device float [nseq * H], index s * H + h), so
+ * that the value of a code x is decode(x) * scale. QK^T and PV run on fp8
+ * MFMA; the probabilities are quantised to E4M3 for PV; out is bf16
+ * [N, H, D]. Otherwise as packed_attn_fwd; the descriptor must have been
+ * built with dtype PVA_FP8_E4M3.
+ */
+int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                        const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
+                        const pva_seg_desc* seg_desc, float scale, void* out, void* stream);
+
+/* Thread-local message of the last failing call on this thread ("" if none). */
+const char* pva_last_error(void);
+
+/* Library version string. */
+const char* pva_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PVA_H_ */

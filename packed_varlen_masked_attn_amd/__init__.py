@@ -1,0 +1,15 @@
+"""Packed variable-length mixed-mask attention for MI355X (gfx950).
+
+The compute path is the C-ABI library ``libpva.so`` (HIP kernels + host
+planner) declared in ``include/pva.h``; this package is its thin binding.
+Importing the package never needs the library; every call that does raises
+if it is missing.
+"""
+from .binding import (PvaError, SegDesc, packed_attn_fwd, packed_attn_fwd_fp8, lib, version, LIB_PATH,
+                      EXPORTED, PVA_OK, PVA_ERR_INVALID_ARG, PVA_ERR_UNSUPPORTED, PVA_ERR_HIP,
+                      PVA_ERR_NO_MEMORY)
+
+__all__ = [
+    "PvaError", "SegDesc", "packed_attn_fwd", "packed_attn_fwd_fp8", "lib", "version", "LIB_PATH", "EXPORTED",
+    "PVA_OK", "PVA_ERR_INVALID_ARG", "PVA_ERR_UNSUPPORTED", "PVA_ERR_HIP", "PVA_ERR_NO_MEMORY",
+]

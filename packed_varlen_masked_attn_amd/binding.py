@@ -1,0 +1,242 @@
+"""ctypes binding of libpva.so: argument marshalling only.
+
+Every step of the attention runs in the library's HIP kernels; this module
+converts torch tensors to device pointers, picks torch's current HIP stream,
+and turns status codes into exceptions. It has no fallback of any kind: if
+the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpva.so")
+
+PVA_OK = 0
+PVA_ERR_INVALID_ARG = -1
+PVA_ERR_UNSUPPORTED = -2
+PVA_ERR_HIP = -3
+PVA_ERR_NO_MEMORY = -4
+DTYPES = {"bf16": 0, "fp8": 1}
+
+EXPORTED = [
+    "pva_seg_desc_build", "pva_seg_desc_build_host", "pva_seg_desc_cu_seqlens", "pva_seg_desc_useful_flops",
+    "pva_seg_desc_tile", "pva_seg_desc_work_items", "pva_seg_desc_free", "packed_attn_fwd",
+    "packed_attn_fwd_fp8", "pva_last_error", "pva_version",
+]
+
+
+class PvaError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"pva status {status}: {message}")
+        self.status = status
+
+
+_lib_handle: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libpva.so once; raise loudly if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m packed_varlen_masked_attn_amd.build` (there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vp = ctypes.c_void_p
+    L.pva_seg_desc_build.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                     vp, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build.restype = ctypes.c_int
+    L.pva_seg_desc_build_host.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build_host.restype = ctypes.c_int
+    L.pva_seg_desc_cu_seqlens.argtypes = [vp, ctypes.POINTER(i32p), i32p]
+    L.pva_seg_desc_cu_seqlens.restype = ctypes.c_int
+    L.pva_seg_desc_useful_flops.argtypes = [vp]
+    L.pva_seg_desc_useful_flops.restype = ctypes.c_int64
+    L.pva_seg_desc_tile.argtypes = [vp, i32p, i32p]
+    L.pva_seg_desc_tile.restype = ctypes.c_int
+    L.pva_seg_desc_work_items.argtypes = [vp, ctypes.POINTER(i32p), i32p]
+    L.pva_seg_desc_work_items.restype = ctypes.c_int
+    L.pva_seg_desc_free.argtypes = [vp]
+    L.pva_seg_desc_free.restype = None
+    L.packed_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    L.packed_attn_fwd.restype = ctypes.c_int
+    L.packed_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    L.packed_attn_fwd_fp8.restype = ctypes.c_int
+    L.pva_last_error.argtypes = []
+    L.pva_last_error.restype = ctypes.c_char_p
+    L.pva_version.argtypes = []
+    L.pva_version.restype = ctypes.c_char_p
+    _lib_handle = L
+    return L
+
+
+def _check(status: int) -> None:
+    if status != PVA_OK:
+        msg = lib().pva_last_error()
+        raise PvaError(status, msg.decode() if msg else "")
+
+
+def _i32_array(xs: Sequence[int]):
+    arr = np.ascontiguousarray(np.asarray(list(xs), dtype=np.int64))
+    if arr.size and (arr.min() < -(2 ** 31) or arr.max() >= 2 ** 31):
+        raise PvaError(PVA_ERR_INVALID_ARG, "length does not fit in int32")
+    arr = arr.astype(np.int32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream_handle(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class SegDesc:
+    """A planned batch composition (segment descriptors + ordered work list).
+
+    Built once per composition and re-used by every launch over it.
+    ``host_only=True`` plans without touching a GPU (for inspection only).
+    """
+
+    def __init__(self, text_len: Sequence[int], image_len: Sequence[int], num_heads: int, head_dim: int,
+                 dtype: str = "bf16", stream=None, host_only: bool = False):
+        if len(text_len) != len(image_len):
+            raise PvaError(PVA_ERR_INVALID_ARG, "text_len and image_len differ in length")
+        if dtype not in DTYPES:
+            raise PvaError(PVA_ERR_INVALID_ARG, f"dtype must be one of {sorted(DTYPES)}")
+        L = lib()
+        t_arr, t_ptr = _i32_array(text_len)
+        i_arr, i_ptr = _i32_array(image_len)
+        h = ctypes.c_void_p()
+        if host_only:
+            st = L.pva_seg_desc_build_host(t_ptr, i_ptr, len(t_arr), int(num_heads), int(head_dim),
+                                           DTYPES[dtype], ctypes.byref(h))
+        else:
+            st = L.pva_seg_desc_build(t_ptr, i_ptr, len(t_arr), int(num_heads), int(head_dim), DTYPES[dtype],
+                                      ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(h))
+        _check(st)
+        self._h = h
+        self.text_len = tuple(int(x) for x in t_arr)
+        self.image_len = tuple(int(x) for x in i_arr)
+        self.num_heads = int(num_heads)
+        self.head_dim = int(head_dim)
+        self.dtype = dtype
+        self.host_only = host_only
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        if self._h is None:
+            raise PvaError(PVA_ERR_INVALID_ARG, "descriptor already freed")
+        return self._h
+
+    @property
+    def nseq(self) -> int:
+        return len(self.text_len)
+
+    @property
+    def cu_seqlens(self) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        _check(lib().pva_seg_desc_cu_seqlens(self.handle, ctypes.byref(p), ctypes.byref(n)))
+        return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
+
+    @property
+    def total_tokens(self) -> int:
+        return int(self.cu_seqlens[-1])
+
+    @property
+    def useful_flops(self) -> int:
+        return int(lib().pva_seg_desc_useful_flops(self.handle))
+
+    @property
+    def tile(self) -> Tuple[int, int]:
+        bm, bn = ctypes.c_int32(), ctypes.c_int32()
+        _check(lib().pva_seg_desc_tile(self.handle, ctypes.byref(bm), ctypes.byref(bn)))
+        return bm.value, bn.value
+
+    @property
+    def work_items(self) -> np.ndarray:
+        """int32 [n_items, 8]: seq, head, q0, q_rows, k_full_end, k_end, T, L (launch order)."""
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        _check(lib().pva_seg_desc_work_items(self.handle, ctypes.byref(p), ctypes.byref(n)))
+        if n.value == 0:
+            return np.zeros((0, 8), np.int32)
+        return np.ctypeslib.as_array(p, shape=(n.value, 8)).copy()
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            lib().pva_seg_desc_free(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_qkvo(desc: SegDesc, tensors, elt_dtypes, out) -> None:
+    import torch
+    N, H, D = desc.total_tokens, desc.num_heads, desc.head_dim
+    for name, t in tensors:
+        if not isinstance(t, torch.Tensor) or not t.is_cuda:
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a device tensor")
+        if t.dtype not in elt_dtypes:
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected one of {elt_dtypes}")
+        if tuple(t.shape) != (N, H, D) or not t.is_contiguous():
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be contiguous [{N}, {H}, {D}], got {tuple(t.shape)}")
+    if not out.is_cuda or out.dtype != torch.bfloat16 or tuple(out.shape) != (N, H, D) or not out.is_contiguous():
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out must be a contiguous device bf16 [{N}, {H}, {D}] tensor")
+
+
+def _check_cu(desc: SegDesc, cu) -> None:
+    import torch
+    if not isinstance(cu, torch.Tensor) or not cu.is_cuda or cu.dtype != torch.int32 or cu.numel() != desc.nseq + 1:
+        raise PvaError(PVA_ERR_INVALID_ARG, f"cu_seqlens must be a device int32 tensor of {desc.nseq + 1} entries")
+
+
+def packed_attn_fwd(q, k, v, cu_seqlens, seg_desc: SegDesc, scale: float, out, stream=None):
+    """bf16 packed mixed-mask attention; writes and returns ``out``."""
+    import torch
+    _check_qkvo(seg_desc, [("q", q), ("k", k), ("v", v)], (torch.bfloat16,), out)
+    _check_cu(seg_desc, cu_seqlens)
+    st = lib().packed_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens), seg_desc.handle,
+                               ctypes.c_float(scale), _ptr(out), ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
+
+
+def packed_attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, seg_desc: SegDesc, scale: float, out,
+                        stream=None):
+    """fp8 (E4M3FN codes + per-(sequence, head) fp32 scales) variant; bf16 ``out``."""
+    import torch
+    _check_qkvo(seg_desc, [("q", q), ("k", k), ("v", v)], (torch.float8_e4m3fn, torch.uint8), out)
+    for name, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
+        if (not s.is_cuda or s.dtype != torch.float32 or s.numel() != seg_desc.nseq * seg_desc.num_heads
+                or not s.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be device float32 [{seg_desc.nseq}, {seg_desc.num_heads}]")
+    _check_cu(seg_desc, cu_seqlens)
+    st = lib().packed_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                   _ptr(cu_seqlens), seg_desc.handle, ctypes.c_float(scale), _ptr(out),
+                                   ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
+
+
+def version() -> str:
+    return lib().pva_version().decode()

@@ -1,0 +1,198 @@
+// C-ABI of the packed mixed-mask attention library: argument validation,
+// descriptor lifetime, error reporting and kernel dispatch.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "pva_internal.h"
+
+namespace pva {
+int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
+                    float scale, void* out, hipStream_t stream);
+int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks,
+                   const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, void* out,
+                   hipStream_t stream);
+}  // namespace pva
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return PVA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int hip_error(hipError_t e, const char* what) {
+  return set_error(PVA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int check_cu(const int32_t* cu, const pva_seg_desc* d, hipStream_t stream) {
+  const char* env = std::getenv("PVA_CHECK");
+  if (!env || std::strcmp(env, "1") != 0) return PVA_OK;
+  std::vector<int32_t> host(d->plan.cu_seqlens.size());
+  hipError_t e = hipMemcpyAsync(host.data(), cu, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_error(e, "PVA_CHECK: reading cu_seqlens");
+  if (host != d->plan.cu_seqlens)
+    return set_error(PVA_ERR_INVALID_ARG, "PVA_CHECK: device cu_seqlens differs from the descriptor's");
+  return PVA_OK;
+}
+
+int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
+                 float scale, void* out, pva_dtype want) {
+  // every check here is host-only and runs before anything touches the device
+  if (!d) return set_error(PVA_ERR_INVALID_ARG, "seg_desc is NULL");
+  if (!q || !k || !v || !out || !cu) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return set_error(PVA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (!(std::isfinite(scale) && scale > 0.0f)) return set_error(PVA_ERR_INVALID_ARG, "scale must be finite and > 0");
+  if (d->plan.dtype != want)
+    return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built for another dtype");
+  if (!d->d_items) return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built host-only and cannot be launched");
+  return PVA_OK;
+}
+
+int build_common(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+                 int32_t head_dim, pva_dtype dtype, bool upload, void* stream, pva_seg_desc** out) {
+  if (!out) return set_error(PVA_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  pva_seg_desc* d = new (std::nothrow) pva_seg_desc();
+  if (!d) return set_error(PVA_ERR_NO_MEMORY, "host allocation failed");
+  std::string err;
+  int st;
+  try {
+    st = pva::build_plan(text_len, image_len, nseq, num_heads, head_dim, dtype, &d->plan, &err);
+  } catch (const std::bad_alloc&) {
+    st = PVA_ERR_NO_MEMORY;
+    err = "host allocation failed";
+  }
+  if (st != PVA_OK) {
+    delete d;
+    return set_error(st, err);
+  }
+  if (upload) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+      delete d;
+      return hip_error(e, "hipGetDevice");
+    }
+    d->device = dev;
+    const size_t bytes = d->plan.items.size() * sizeof(pva::WorkItem);
+    if (bytes > 0) {
+      e = hipMalloc(&d->d_items, bytes);
+      if (e != hipSuccess) {
+        d->d_items = nullptr;
+        delete d;
+        return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
+      }
+      e = hipMemcpyAsync(d->d_items, d->plan.items.data(), bytes, hipMemcpyHostToDevice,
+                         static_cast<hipStream_t>(stream));
+      if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+      if (e != hipSuccess) {
+        (void)hipFree(d->d_items);
+        delete d;
+        return hip_error(e, "uploading the work list");
+      }
+    } else {
+      // every launch is empty; keep a non-null marker so the descriptor is launchable
+      d->d_items = reinterpret_cast<void*>(uintptr_t(1));
+    }
+  }
+  *out = d;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+                       int32_t head_dim, pva_dtype dtype, void* stream, pva_seg_desc** out) {
+  return build_common(text_len, image_len, nseq, num_heads, head_dim, dtype, true, stream, out);
+}
+
+int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+                            int32_t head_dim, pva_dtype dtype, pva_seg_desc** out) {
+  return build_common(text_len, image_len, nseq, num_heads, head_dim, dtype, false, nullptr, out);
+}
+
+int pva_seg_desc_cu_seqlens(const pva_seg_desc* d, const int32_t** host_cu, int32_t* len) {
+  if (!d || !host_cu || !len) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
+  *host_cu = d->plan.cu_seqlens.data();
+  *len = static_cast<int32_t>(d->plan.cu_seqlens.size());
+  return ok();
+}
+
+int64_t pva_seg_desc_useful_flops(const pva_seg_desc* d) { return d ? d->plan.useful_flops : -1; }
+
+int pva_seg_desc_tile(const pva_seg_desc* d, int32_t* block_m, int32_t* block_n) {
+  if (!d || !block_m || !block_n) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
+  *block_m = d->plan.tile.bm;
+  *block_n = d->plan.tile.bn;
+  return ok();
+}
+
+int pva_seg_desc_work_items(const pva_seg_desc* d, const int32_t** items, int32_t* n_items) {
+  if (!d || !items || !n_items) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
+  *items = reinterpret_cast<const int32_t*>(d->plan.items.data());
+  *n_items = static_cast<int32_t>(d->plan.items.size());
+  return ok();
+}
+
+void pva_seg_desc_free(pva_seg_desc* d) {
+  if (!d) return;
+  if (d->d_items && d->d_items != reinterpret_cast<void*>(uintptr_t(1))) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != d->device && d->device >= 0) (void)hipSetDevice(d->device);
+    (void)hipFree(d->d_items);
+    if (cur >= 0 && cur != d->device) (void)hipSetDevice(cur);
+  }
+  delete d;
+}
+
+int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
+                    const pva_seg_desc* seg_desc, float scale, void* out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_seqlens, seg_desc, scale, out, PVA_BF16);
+  if (st != PVA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = check_cu(cu_seqlens, seg_desc, s)) != PVA_OK) return st;
+  st = pva::launch_fwd_bf16(q, k, v, cu_seqlens, seg_desc, scale, out, s);
+  if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
+  return ok();
+}
+
+int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
+                        const float* v_scale, const int32_t* cu_seqlens, const pva_seg_desc* seg_desc, float scale,
+                        void* out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_seqlens, seg_desc, scale, out, PVA_FP8_E4M3);
+  if (st != PVA_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = check_cu(cu_seqlens, seg_desc, s)) != PVA_OK) return st;
+  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, seg_desc, scale, out, s);
+  if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
+  if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
+  return ok();
+}
+
+const char* pva_last_error(void) { return g_last_error.c_str(); }
+
+const char* pva_version(void) { return "pva 0.1 gfx950"; }
+
+}  // extern "C"

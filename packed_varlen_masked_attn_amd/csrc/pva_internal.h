@@ -1,0 +1,69 @@
+// Internal declarations shared by the planner, the C-ABI layer and the kernels.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/pva.h"
+
+#if defined(__HIPCC__)
+#define PVA_HOST_DEVICE __host__ __device__
+#else
+#define PVA_HOST_DEVICE
+#endif
+
+namespace pva {
+
+// One record of the device work list: a (sequence, head, query tile).
+// k_full_end / k_end are key-tile indices: tiles [0, k_full_end) need no mask,
+// [k_full_end, k_end) are masked element-wise, tiles >= k_end are never read.
+struct WorkItem {
+  int32_t seq;     // -1: empty slot (keeps the XCD alignment of the list)
+  int32_t head;
+  int32_t q0;      // first query row of the tile, relative to the sequence start
+  int32_t q_rows;  // valid rows in the tile (<= BM)
+  int32_t k_full_end;
+  int32_t k_end;
+  int32_t text_len;
+  int32_t seq_len;
+};
+static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
+
+// Tile shape used by the kernels for a given element type and head size.
+struct TileShape {
+  int32_t bm;  // query rows per work item
+  int32_t bn;  // keys per streamed tile
+};
+TileShape tile_shape(pva_dtype dtype, int32_t head_dim);
+
+// Number of XCDs whose L2 caches the scheduler groups work for.
+constexpr int kNumXcd = 8;
+
+struct Plan {
+  pva_dtype dtype = PVA_BF16;
+  int32_t nseq = 0, num_heads = 0, head_dim = 0;
+  TileShape tile{0, 0};
+  std::vector<int32_t> text_len, image_len, seq_len, cu_seqlens;
+  std::vector<WorkItem> items;  // launch order, XCD-interleaved, padded with empty slots
+  int64_t useful_flops = 0;
+  int64_t total_tokens = 0;
+};
+
+// Mask key limit of row i of a sequence: keys [0, lim) are allowed.
+PVA_HOST_DEVICE inline int32_t key_limit(int32_t i, int32_t text_len, int32_t seq_len) {
+  return i < text_len ? i + 1 : seq_len;
+}
+
+// Validates and plans; on failure returns a status and fills `err`.
+int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+               int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err);
+
+}  // namespace pva
+
+// The descriptor handed across the C-ABI.
+struct pva_seg_desc {
+  pva::Plan plan;
+  void* d_items = nullptr;  // device copy of plan.items (nullptr for host-only descriptors)
+  int32_t device = -1;      // HIP device the work list lives on
+};

@@ -1,0 +1,151 @@
+"""The C-ABI library loads on a machine without a GPU, exports every symbol
+include/pva.h declares, and rejects every invalid argument on the host
+before anything reaches a device. No kernel is launched here."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import packed_varlen_masked_attn_amd as pva
+from packed_varlen_masked_attn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pva.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("defined",)))
+
+
+def test_library_built():
+    assert os.path.exists(pva.LIB_PATH), "run `python -m packed_varlen_masked_attn_amd.build` first"
+
+
+def test_header_symbols_exported():
+    names = header_functions()
+    assert "packed_attn_fwd" in names and "pva_seg_desc_build" in names
+    L = pva.lib()
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in pva.h but not exported"
+    out = subprocess.run(["nm", "-D", "--defined-only", pva.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in names:
+        assert n in exported
+    assert sorted(binding.EXPORTED) == names
+
+
+def test_version():
+    assert "gfx950" in pva.version()
+
+
+def _build_host(t, i, H=2, D=128, dtype=0):
+    t_arr = np.asarray(t, np.int32)
+    i_arr = np.asarray(i, np.int32)
+    h = ctypes.c_void_p()
+    st = pva.lib().pva_seg_desc_build_host(t_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                           i_arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                           len(t_arr), H, D, dtype, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("t,i,H,D,dtype,code", [
+    ([], [], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),             # nseq = 0
+    ([-1], [4], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),          # T < 0
+    ([4], [-2], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),          # I < 0
+    ([0], [0], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),           # L = 0
+    ([4], [4], 0, 128, 0, pva.PVA_ERR_INVALID_ARG),           # H = 0
+    ([4], [4], 2, 96, 0, pva.PVA_ERR_UNSUPPORTED),            # D not in {64, 128}
+    ([4], [4], 2, 64, 1, pva.PVA_ERR_UNSUPPORTED),            # fp8 with D = 64
+    ([4], [4], 2, 128, 7, pva.PVA_ERR_INVALID_ARG),           # unknown dtype
+    ([2 ** 30, 2 ** 30], [0, 1], 1, 64, 0, pva.PVA_ERR_INVALID_ARG),  # N overflows int32
+])
+def test_build_rejects(t, i, H, D, dtype, code):
+    if t:
+        st, h = _build_host(t, i, H, D, dtype)
+    else:  # valid arrays, nseq = 0
+        one = np.asarray([4], np.int32)
+        ptr = one.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+        h = ctypes.c_void_p()
+        st = pva.lib().pva_seg_desc_build_host(ptr, ptr, 0, H, D, dtype, ctypes.byref(h))
+    assert st == code
+    assert h.value is None
+    assert pva.lib().pva_last_error()
+
+
+def test_build_null_pointers():
+    h = ctypes.c_void_p()
+    t = np.asarray([3], np.int32)
+    assert pva.lib().pva_seg_desc_build_host(None, t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 2, 128, 0,
+                                             ctypes.byref(h)) == pva.PVA_ERR_INVALID_ARG
+    assert pva.lib().pva_seg_desc_build_host(t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                             t.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), 1, 2, 128, 0,
+                                             None) == pva.PVA_ERR_INVALID_ARG
+
+
+def test_binding_errors_raise():
+    with pytest.raises(pva.PvaError) as e:
+        pva.SegDesc([4], [4], 2, 96, host_only=True)
+    assert e.value.status == pva.PVA_ERR_UNSUPPORTED
+    with pytest.raises(pva.PvaError):
+        pva.SegDesc([4, 2], [4], 2, 128, host_only=True)
+
+
+FAKE = 0x100000  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("case", ["null_desc", "null_q", "misaligned_k", "nan_scale", "neg_scale", "zero_scale",
+                                  "inf_scale", "wrong_dtype", "host_only"])
+def test_fwd_rejects_on_host(case):
+    L = pva.lib()
+    desc = pva.SegDesc([16, 16], [48, 48], 2, 64, dtype="bf16", host_only=True)
+    d = desc.handle
+    q = k = v = out = cu = ctypes.c_void_p(FAKE)
+    scale = 0.125
+    if case == "null_desc":
+        d = None
+    elif case == "null_q":
+        q = None
+    elif case == "misaligned_k":
+        k = ctypes.c_void_p(FAKE + 8)
+    elif case == "nan_scale":
+        scale = math.nan
+    elif case == "neg_scale":
+        scale = -0.1
+    elif case == "zero_scale":
+        scale = 0.0
+    elif case == "inf_scale":
+        scale = math.inf
+    if case == "wrong_dtype":
+        st = L.packed_attn_fwd_fp8(q, k, v, cu, cu, cu, cu, d, ctypes.c_float(scale), out, None)
+    else:
+        st = L.packed_attn_fwd(q, k, v, cu, d, ctypes.c_float(scale), out, None)
+    assert st == pva.PVA_ERR_INVALID_ARG
+    msg = L.pva_last_error().decode()
+    assert msg
+    if case == "host_only":
+        assert "host-only" in msg
+    desc.close()
+
+
+def test_fp8_scale_pointers_checked():
+    L = pva.lib()
+    desc = pva.SegDesc([8], [8], 2, 128, dtype="fp8", host_only=True)
+    p = ctypes.c_void_p(FAKE)
+    st = L.packed_attn_fwd_fp8(p, p, p, None, p, p, p, desc.handle, ctypes.c_float(0.1), p, None)
+    assert st == pva.PVA_ERR_INVALID_ARG
+
+
+def test_accessor_null_args():
+    L = pva.lib()
+    assert L.pva_seg_desc_useful_flops(None) == -1
+    assert L.pva_seg_desc_tile(None, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_seg_desc_cu_seqlens(None, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_seg_desc_work_items(None, None, None) == pva.PVA_ERR_INVALID_ARG
+    L.pva_seg_desc_free(None)  # no-op
