@@ -53,7 +53,22 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--kernel-only", action="store_true", help="time the kernel only (for profilers)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain copy kernel of known size: 1 GiB read + 1 GiB written per launch."""
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -68,6 +83,9 @@ def main():
     import packed_varlen_masked_attn_amd as pva
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]()
     is_fp8 = w.dtype == "fp8"

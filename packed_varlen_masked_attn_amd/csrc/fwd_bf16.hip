@@ -6,25 +6,39 @@
 // challenge) and Model structure item 1 (Generalized Causal Attention: causal
 // text prefix, bidirectional image block that sees the whole prefix).
 //
-// One workgroup = 4 waves = one work item (sequence, head, 128 query rows);
-// each wave owns 32 query rows. Key/value tiles of 64 keys are streamed
-// through double-buffered LDS, the next tile's global loads in flight while
-// the current one is consumed.
+// One workgroup = 4 waves = one work item (sequence, head, 256 query rows);
+// one wave per SIMD, each owning 64 query rows as two 32-row blocks that share
+// every K and V operand read. Keys are streamed in tiles of 32.
 //
-// Per wave and key tile, on 32x32x16 bf16 MFMA:
+// Per wave and key tile j, on 32x32x16 bf16 MFMA:
 //   S^T[key, q] = K Q^T    A = K from LDS (16-byte reads), B = Q^T held in
 //                          registers for the whole item. Each lane then owns
-//                          one query column and 16 keys per 32-key block, so
-//                          row max / row sum are in-lane plus one exchange
-//                          between the two 32-lane halves.
+//                          one query column of each block, so row max and
+//                          row sum are in-lane plus one exchange between the
+//                          two 32-lane halves.
 //   online softmax in fp32, log2 domain, lazy rescaling of O and l.
 //   O^T[d, q] += V^T P^T   B = P^T straight from the S^T accumulators (cast to
 //                          bf16, no shuffle: the contraction order of the keys
 //                          is permuted instead), A = V^T read from the
 //                          row-major V tile with ds_read_b64_tr_b16.
-// Tiles the mask fully hides are never loaded; tiles it fully allows skip the
-// element mask.
+//
+// Software pipeline (iteration j, one barrier each):
+//   issue global->LDS loads of K(j+NS) and V(j+NS-1) (direct LDS DMA)
+//   [S(j+1) MFMAs]  interleaved with  [exp / row sums / bf16 cast of tile j]
+//   (partial tiles only) element mask of tile j+1
+//   [PV(j) MFMAs]   interleaved with  [row max of tile j+1]
+//   rare branch: rescale O and l when a row's reference max moved
+//   wait for the loads of K(j+2) and V(j+1) only; later ones stay in flight
+// K and V each have a ring of NS LDS stages, so every load has NS-1
+// iterations to land. Tiles the mask fully hides are never loaded; tiles it
+// fully allows skip the element mask.
+#include <type_traits>
+
 #include "kernel_common.h"
+
+#ifndef PVA_BF16_QB
+#define PVA_BF16_QB 1  // 32-row query blocks per wave: 1 (2 waves/SIMD) or 2 (1 wave/SIMD)
+#endif
 
 namespace pva {
 
@@ -32,195 +46,477 @@ namespace {
 
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = 128, BN = 64, NW = 4, NT = 256;
-  static constexpr int C = D / 8;     // 16-byte chunks per K/V row
-  static constexpr int NKC = D / 16;  // MFMA k-steps over the head dimension for S^T
-  static constexpr int NDB = D / 32;  // 32-row blocks of O^T
-  static constexpr int TILE_BYTES = BN * D * 2;
-  static constexpr int NLD = BN * C / NT;  // 16-byte loads per thread per tensor per tile
-  static constexpr int SMEM = 2 * 2 * TILE_BYTES;  // double-buffered K and V
+  static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = 4, NT = 256;
+  static constexpr int QB = PVA_BF16_QB;   // 32-row query blocks per wave
+  static_assert(BM == NW * QB * 32 && BN == 32, "4 waves x 64 query rows; 32-key tiles");
+  static constexpr int C = D / 8;          // 16-byte chunks per K/V row
+  static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
+  static constexpr int NDB = D / 32;       // 32-row blocks of O^T
+  static constexpr int TILE = BN * D * 2;  // bytes of one K or V tile
+  static constexpr int NLD = BN * C / NT;  // 16-byte DMA rounds per thread per tile and tensor
+  static_assert(NLD >= 1 && BN * C % NT == 0, "whole DMA rounds");
+  static constexpr int NS = 4;             // LDS stages per tensor
+};
+
+// s_waitcnt with vmcnt = N and the other counters untouched (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the global-memory fence __syncthreads() implies
+// (that fence would also wait for every DMA still in flight). LDS reads issued
+// before it have been consumed by then; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Per-lane state of the online softmax for one query column.
+struct RowState {
+  float m;  // reference max (log2 units); O and l are relative to it
+  float l;  // this lane's partial row sum (the other half-wave holds the rest)
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
+struct Kernel {
+  using Cfg = Bf16Cfg<D>;
+  static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD;
+  typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+  // ---- global -> LDS (direct DMA). Lane writes 16 B at stage + 16 * slot;
+  // slot s holds row s / C, stored chunk s % C = global chunk (s % C) ^
+  // swizzle(row). Rows past the sequence end are clamped to its last row
+  // (finite data; the mask discards them).
+  template <bool IS_V>
+  static __device__ __forceinline__ void load_tile(const uint8_t* seq_base, int k0, int L, int64_t rs2,
+                                                   uint8_t* stage, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      const int s = Cfg::NT * i + 64 * wave + lane;
+      const int r = s / C, p = s % C;
+      const int c = p ^ (IS_V ? swz_v<C>(r) : swz_k<C>(r));
+      const int row = min(k0 + r, L - 1);
+      const uint8_t* src = seq_base + int64_t(row) * rs2 + 16 * c;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (PVA_LDS void*)(stage + 16 * (Cfg::NT * i + 64 * wave)), 16, 0, 0);
+    }
+  }
+
+  // ---- K operands of one tile: row l32, chunk 2c + g (swizzled by row)
+  static __device__ __forceinline__ void read_k(bf16x8 (&a)[NKC], const uint8_t* kst, int l32, int g) {
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+      a[c] = *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * C + ((2 * c + g) ^ swz_k<C>(l32))));
+  }
+
+  // ---- V^T operands of one tile: for 16-key step kc and 32-column block db
+  static __device__ __forceinline__ void read_v(s16x8 (&a)[2][NDB], const uint8_t* vst, int v_row0, int v_col) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + v_col;
+        const int chunk = col >> 3, boff = 2 * (col & 7);
+        const int r0 = 16 * kc + v_row0, r1 = r0 + 8;
+        const uint8_t* p0 = vst + 16 * (r0 * C + (chunk ^ swz_v<C>(r0))) + boff;
+        const uint8_t* p1 = vst + 16 * (r1 * C + (chunk ^ swz_v<C>(r1))) + boff;
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
+        a[kc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      }
+  }
+
+  // ---- S^T = K Q^T for both query blocks (two independent MFMA chains)
+  static __device__ __forceinline__ void s_mfma(f32x16 (&s)[QB], const bf16x8 (&a)[NKC],
+                                                const bf16x8 (&qf)[QB][NKC]) {
+#pragma unroll
+    for (int h = 0; h < QB; ++h) s[h] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c)
+#pragma unroll
+      for (int h = 0; h < QB; ++h) s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], qf[h][c], s[h], 0, 0, 0);
+  }
+
+  // ---- O^T += V^T P^T for both query blocks
+  static __device__ __forceinline__ void pv_mfma(f32x16 (&o)[QB][NDB], const s16x8 (&a)[2][NDB],
+                                                 const bf16x8 (&pb)[QB][2]) {
+#pragma unroll
+    for (int kc = 0; kc < 2; ++kc)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int h = 0; h < QB; ++h)
+          o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kc][db]), pb[h][kc],
+                                                             o[h][db], 0, 0, 0);
+  }
+
+  // ---- instruction interleaving hints for the scheduler (same basic block)
+  // masks: 0x008 MFMA, 0x002 VALU, 0x080 any LDS, 0x100 LDS read
+  static __device__ __forceinline__ void schedule_s_with_exp() {
+    __builtin_amdgcn_sched_group_barrier(0x100, NKC, 0);
+#pragma unroll
+    for (int i = 0; i < QB * NKC; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
+    }
+  }
+  static __device__ __forceinline__ void schedule_pv_with_max() {
+    __builtin_amdgcn_sched_group_barrier(0x080, 4 * NDB, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * QB * NDB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    }
+  }
+
+  // ---- an empty asm that consumes the probabilities: the compiler must have
+  // them in registers at this point, so it cannot sink their computation past
+  // the following branch into the PV block
+  static __device__ __forceinline__ void pin(bf16x8 (&pb)[QB][2], float (&psum)[QB]) {
+#pragma unroll
+    for (int h = 0; h < QB; ++h) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        i32x4 v = __builtin_bit_cast(i32x4, pb[h][k]);
+        asm volatile("" : "+v"(v));
+        pb[h][k] = __builtin_bit_cast(bf16x8, v);
+      }
+      asm volatile("" : "+v"(psum[h]));
+    }
+  }
+
+  // ---- S(j+1) = K Q^T for both query blocks, interleaved in program order
+  // with the probabilities of tile j: per d-chunk c, one K read two chunks
+  // ahead, two MFMAs (one per query block), then four exponentials.
+  static __device__ __forceinline__ void s_with_probs(f32x16 (&snext)[QB], const uint8_t* kst,
+                                                      const bf16x8 (&qf)[QB][NKC], const f32x16 (&scur)[QB],
+                                                      float scale_log2, const RowState (&st)[QB],
+                                                      bf16x8 (&pb)[QB][2], float (&psum)[QB], int l32, int g) {
+    constexpr int PER_C = (QB * 16 + NKC - 1) / NKC;  // exponentials per d-chunk
+    const uint8_t* krow = kst + 16 * l32 * C;
+    const int sw = swz_k<C>(l32);
+    auto rd = [&](int c) { return *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * c + g) ^ sw)); };
+    bf16x8 ka[3];
+    ka[0] = rd(0);
+    if (NKC > 1) ka[1] = rd(1);
+#pragma unroll
+    for (int h = 0; h < QB; ++h) snext[h] = f32x16{};
+    float part[QB][4];
+#pragma unroll
+    for (int h = 0; h < QB; ++h)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) part[h][k] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (c + 2 < NKC) ka[(c + 2) % 3] = rd(c + 2);
+#pragma unroll
+      for (int h = 0; h < QB; ++h)
+        snext[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % 3], qf[h][c], snext[h], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < PER_C; ++e) {
+        const int idx = c * PER_C + e;  // element of the (QB x 16) probability tile
+        if (idx < QB * 16) {
+          const int h = idx / 16, i = idx % 16;
+          const float p = fast_exp2(fmaf(scur[h][i], scale_log2, -st[h].m));
+          part[h][i % 4] += p;
+          pb[h][i / 8][i % 8] = (__bf16)p;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < QB; ++h) psum[h] = (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
+    pin(pb, psum);
+  }
+
+  // ---- O^T += V^T P^T for both query blocks, interleaved in program order
+  // with the row max of tile j+1: per (kc, db) step, one V^T operand read two
+  // steps ahead, two MFMAs, then a few max operations.
+  static __device__ __forceinline__ void pv_with_max(f32x16 (&o)[QB][NDB], const uint8_t* vst,
+                                                     const bf16x8 (&pb)[QB][2], const f32x16 (&snext)[QB],
+                                                     float scale_log2, float (&mt)[QB], int v_row0, int v_col) {
+    constexpr int NSTEP = 2 * NDB;
+    auto rd = [&](int step) {
+      const int kc = step / NDB, db = step % NDB;
+      const int col = 32 * db + v_col;
+      const int chunk = col >> 3, boff = 2 * (col & 7);
+      const int r0 = 16 * kc + v_row0, r1 = r0 + 8;
+      const uint8_t* p0 = vst + 16 * (r0 * C + (chunk ^ swz_v<C>(r0))) + boff;
+      const uint8_t* p1 = vst + 16 * (r1 * C + (chunk ^ swz_v<C>(r1))) + boff;
+      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
+      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
+      return s16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    s16x8 va[3];
+    va[0] = rd(0);
+    va[1] = rd(1);
+    float mx[QB];
+#pragma unroll
+    for (int h = 0; h < QB; ++h) mx[h] = snext[h][0];
+    constexpr int PER_STEP = (QB * 15 + NSTEP - 1) / NSTEP;
+#pragma unroll
+    for (int step = 0; step < NSTEP; ++step) {
+      if (step + 2 < NSTEP) va[(step + 2) % 3] = rd(step + 2);
+      const int kc = step / NDB, db = step % NDB;
+#pragma unroll
+      for (int h = 0; h < QB; ++h)
+        o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[step % 3]), pb[h][kc],
+                                                           o[h][db], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < PER_STEP; ++e) {
+        const int idx = step * PER_STEP + e;  // element 1..15 of each block's max
+        if (idx < QB * 15) {
+          const int h = idx / 15, i = 1 + idx % 15;
+          mx[h] = fmaxf(mx[h], snext[h][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < QB; ++h) mt[h] = half_swap_max(mx[h]) * scale_log2;
+  }
+
+  // ---- element mask: keys at or past a lane's limit get -inf
+  static __device__ __forceinline__ void mask(f32x16 (&s)[QB], int k0, int g, const int (&mylim)[QB]) {
+#pragma unroll
+    for (int h = 0; h < QB; ++h)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i / 4) + 4 * g + (i % 4);
+        if (key >= mylim[h]) s[h][i] = -INFINITY;
+      }
+  }
+
+  // ---- tile max in log2 units per block, shared by both half-waves
+  static __device__ __forceinline__ void tile_max(const f32x16 (&s)[QB], float scale_log2, float (&mt)[QB]) {
+#pragma unroll
+    for (int h = 0; h < QB; ++h) {
+      float mx = s[h][0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
+      mt[h] = half_swap_max(mx) * scale_log2;
+    }
+  }
+
+  // ---- probabilities of a tile (bf16 B operands of PV) and their fp32 sums
+  static __device__ __forceinline__ void probs(const f32x16 (&s)[QB], float scale_log2, const RowState (&st)[QB],
+                                               bf16x8 (&pb)[QB][2], float (&psum)[QB]) {
+#pragma unroll
+    for (int h = 0; h < QB; ++h) {
+      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // short dependency chains
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(s[h][i], scale_log2, -st[h].m));
+        part[i % 4] += p;
+        pb[h][i / 8][i % 8] = (__bf16)p;
+      }
+      psum[h] = (part[0] + part[1]) + (part[2] + part[3]);
+    }
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
                                                           const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V,
                                                           const int32_t* __restrict__ cu,
                                                           const WorkItem* __restrict__ items, int H,
                                                           float scale_log2, __bf16* __restrict__ O) {
-  using Cfg = Bf16Cfg<D>;
-  constexpr int BN = Cfg::BN, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD;
-  constexpr int TB = Cfg::TILE_BYTES;
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using Kn = Kernel<D>;
+  using Cfg = typename Kn::Cfg;
+  using s16x8 = typename Kn::s16x8;
+  constexpr int BN = Cfg::BN, QB = Cfg::QB, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD, NS = Cfg::NS;
+  static_assert(NS == 4, "the loop below is unrolled for a ring of four stages");
+  // separate arrays per stage: the compiler sees that an LDS DMA into one
+  // stage and reads of another do not alias
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::TILE], k1s[Cfg::TILE], k2s[Cfg::TILE], k3s[Cfg::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::TILE], v1s[Cfg::TILE], v2s[Cfg::TILE], v3s[Cfg::TILE];
+  uint8_t* const kst[NS] = {k0s, k1s, k2s, k3s};
+  uint8_t* const vst[NS] = {v0s, v1s, v2s, v3s};
 
   const WorkItem it = items[blockIdx.x];
   if (it.seq < 0) return;  // empty slot; uniform over the workgroup
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform per wave; reading it through a scalar register
+  // makes every per-wave condition below a scalar branch
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int T = it.text_len, L = it.seq_len;
   const int64_t rs = int64_t(H) * D;  // elements between consecutive tokens of one head
+  const int64_t rs2 = rs * 2;         // bytes
   const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
   const __bf16* Qh = Q + base;
-  const __bf16* Kh = K + base;
-  const __bf16* Vh = V + base;
+  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
+  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + base);
 
-  // this lane's query row and its key limit; rows past the sequence end act
-  // as image rows (their outputs are never stored)
-  const int qrow = it.q0 + 32 * wave + l32;
-  const int mylim = key_limit(qrow, T, L);
-  const int wrow0 = it.q0 + 32 * wave;
-  const bool wave_active = wrow0 < L;
-  const int wlim_min = key_limit(wrow0, T, L);
-  const int wlim_max = wave_active ? key_limit(min(wrow0 + 31, L - 1), T, L) : 0;
-
-  // Q^T operand: chunk c holds d = 16c + 8g .. +7 of this lane's query row
-  bf16x8 qf[NKC];
+  // this lane's query rows (one per block) and their key limits; rows past
+  // the sequence end act as image rows (their outputs are never stored)
+  const int wrow0 = it.q0 + 32 * QB * wave;
+  int qrow[QB], mylim[QB];
 #pragma unroll
-  for (int c = 0; c < NKC; ++c) {
-    if (qrow < L)
-      qf[c] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(qrow) * rs + 16 * c + 8 * g);
-    else
-      qf[c] = bf16x8{};
+  for (int h = 0; h < QB; ++h) {
+    qrow[h] = wrow0 + 32 * h + l32;
+    mylim[h] = key_limit(qrow[h], T, L);
   }
+  const int wlim_min = key_limit(wrow0, T, L);  // smallest key limit of the wave's rows
+  const int kend = it.k_end;
 
-  uint4 kst[NLD], vst[NLD];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BN;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int u = tid + Cfg::NT * i, r = u / C, c = u % C, key = k0 + r;
-      if (key < L) {
-        kst[i] = *reinterpret_cast<const uint4*>(Kh + int64_t(key) * rs + 8 * c);
-        vst[i] = *reinterpret_cast<const uint4*>(Vh + int64_t(key) * rs + 8 * c);
-      } else {
-        kst[i] = uint4{0, 0, 0, 0};
-        vst[i] = uint4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-    uint8_t* kb = smem + buf * 2 * TB;
-    uint8_t* vb = kb + TB;
-#pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int u = tid + Cfg::NT * i, r = u / C, c = u % C;
-      *reinterpret_cast<uint4*>(kb + 16 * (r * C + (c ^ swz_k<C>(r)))) = kst[i];
-      *reinterpret_cast<uint4*>(vb + 16 * (r * C + (c ^ swz_v<C>(r)))) = vst[i];
-    }
-  };
+  // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
+  auto ld_k = [&](int t, uint8_t* stage) { Kn::template load_tile<false>(Kb, t * BN, L, rs2, stage, wave, lane); };
+  auto ld_v = [&](int t, uint8_t* stage) { Kn::template load_tile<true>(Vb, t * BN, L, rs2, stage, wave, lane); };
+  if (kend > 0) ld_k(0, kst[0]);
+  if (kend > 1) ld_k(1, kst[1]);
+  if (kend > 0) ld_v(0, vst[0]);
+  if (kend > 2) ld_k(2, kst[2]);
+  if (kend > 1) ld_v(1, vst[1]);
+  if (kend > 3) ld_k(3, kst[3]);
+  if (kend > 2) ld_v(2, vst[2]);
 
-  f32x16 oacc[NDB];
+  // Q^T operands: chunk c holds d = 16c + 8g .. +7 of this lane's query rows
+  bf16x8 qf[QB][NKC];
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int h = 0; h < QB; ++h)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (qrow[h] < L)
+        qf[h][c] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(qrow[h]) * rs + 16 * c + 8 * g);
+      else
+        qf[h][c] = bf16x8{};
+    }
+
+  f32x16 oacc[QB][NDB];
+#pragma unroll
+  for (int h = 0; h < QB; ++h)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[h][db] = f32x16{};
+  RowState st[QB];
+#pragma unroll
+  for (int h = 0; h < QB; ++h) st[h] = RowState{-INFINITY, 0.0f};
 
   // per-lane constant parts of the V^T (transpose-read) addresses
   const int v_row0 = 4 * g + (lane & 15) / 4;
   const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  const int kend = it.k_end;
+  // K0, K1, V0 must have landed; K2 V1 K3 V2 may still be in flight
+  if (kend > 3)
+    wait_vmcnt<4 * NLD>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+
+  f32x16 sa[QB], sb[QB];
+  // S(0) and its reference max. Rows past the sequence end, and tiles past a
+  // row's key limit, are computed masked: their probabilities are exactly
+  // zero. That keeps every branch in the loop scalar and rare.
   if (kend > 0) {
-    gload(0);
-    sstore(0);
+    bf16x8 ka[NKC];
+    Kn::read_k(ka, kst[0], l32, g);
+    Kn::s_mfma(sa, ka, qf);
+    if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
+    float mt[QB];
+    Kn::tile_max(sa, scale_log2, mt);
+#pragma unroll
+    for (int h = 0; h < QB; ++h) st[h].m = mt[h];  // first tile: O and l are still zero
   }
-  __syncthreads();
-  for (int kt = 0; kt < kend; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < kend) gload(kt + 1);
-    const int k0 = kt * BN;
-    if (k0 < wlim_max) {
-      const uint8_t* kb = smem + buf * 2 * TB;
-      const uint8_t* vb = kb + TB;
-      // ---- S^T = K Q^T for keys k0 .. k0+63 (two 32-key blocks)
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+
+  // Steady-state iteration j (j + 1 < kend); `scur` holds S(j), `snext`
+  // receives S(j+1). SJ = j % NS (compile-time in each unrolled copy).
+  auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[QB], f32x16(&snext)[QB]) {
+    constexpr int SJ = decltype(sj_tag)::value;
+    lds_barrier();  // every wave is done with S(j) (K stage SJ) and PV(j-1) (V stage SJ-1)
+    const bool steady = j + NS < kend;
+    if (steady) ld_k(j + NS, kst[SJ]);
+    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
+    const int k1 = (j + 1) * BN;
+    // S(j+1) MFMAs interleaved with the exponentials of tile j
+    bf16x8 pb[QB][2];
+    float psum[QB];
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st, pb, psum, l32, g);
 #pragma unroll
-      for (int c = 0; c < NKC; ++c) {
+    for (int h = 0; h < QB; ++h) st[h].l += psum[h];
+    if (k1 + BN > wlim_min) Kn::mask(snext, k1, g, mylim);
+    // PV(j) MFMAs interleaved with the row max of tile j+1
+    float mt[QB];
+    Kn::pv_with_max(oacc, vst[SJ], pb, snext, scale_log2, mt, v_row0, v_col);
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int r = 32 * b + l32;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kb + 16 * (r * C + ((2 * c + g) ^ swz_k<C>(r))));
-          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[c], sacc[b], 0, 0, 0);
-        }
-      }
-      // ---- element mask on tiles the mask does not fully allow for this wave
-      if (k0 + BN > wlim_min) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * b + 8 * (i / 4) + 4 * g + (i % 4);
-            if (key >= mylim) sacc[b][i] = -INFINITY;
-          }
-      }
-      // ---- online softmax (log2 domain)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[b][i]);
-      mx = half_swap_max(mx);
-      const float mt = mx * scale_log2;
-      const bool need = mt > m_run + kLazyRescale;
+    for (int h = 0; h < QB; ++h) {
+      const bool need = mt[h] > st[h].m + kLazyRescale;
       if (wave_any(need)) {
         // per-lane decision: a lane that does not need it keeps its max (alpha = 1
         // exactly), so each row's arithmetic depends on its own scores only
-        const float mnew = need ? mt : m_run;
-        const float alpha = need ? fast_exp2(m_run - mnew) : 1.0f;
+        const float alpha = need ? fast_exp2(st[h].m - mt[h]) : 1.0f;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-        l_run *= alpha;
-        m_run = mnew;
-      }
-      bf16x8 pb[4];
-      float psum = 0.0f;
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(fmaf(sacc[b][i], scale_log2, -m_run));
-          psum += p;
-          pb[2 * b + i / 8][i % 8] = (__bf16)p;
-        }
-      l_run += psum;
-      // ---- O^T += V^T P^T, 16 keys per MFMA step
-#pragma unroll
-      for (int kc = 0; kc < 4; ++kc) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int col = 32 * db + v_col;
-          const int chunk = col >> 3, boff = 2 * (col & 7);
-          const int r0 = 16 * kc + v_row0, r1 = r0 + 8;
-          const uint8_t* p0 = vb + 16 * (r0 * C + (chunk ^ swz_v<C>(r0))) + boff;
-          const uint8_t* p1 = vb + 16 * (r1 * C + (chunk ^ swz_v<C>(r1))) + boff;
-          const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
-          const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
-          typedef short s16x8 __attribute__((ext_vector_type(8)));
-          const s16x8 a16 = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          const bf16x8 a = __builtin_bit_cast(bf16x8, a16);
-          oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[kc], oacc[db], 0, 0, 0);
-        }
+          for (int i = 0; i < 16; ++i) oacc[h][db][i] *= alpha;
+        st[h].l *= alpha;
+        st[h].m = need ? mt[h] : st[h].m;
       }
     }
-    if (kt + 1 < kend) sstore(buf ^ 1);
-    __syncthreads();
+    // K(j+2) and V(j+1) are needed next; the loads of iterations j-1 and j
+    // (2 tiles x 2 tensors x NLD each) may stay in flight in steady state
+    if (steady)
+      wait_vmcnt<4 * NLD>();
+    else
+      wait_vmcnt<0>();
+  };
+  // Last iteration: probabilities and PV of the final tile only.
+  auto last = [&](auto sj_tag, f32x16(&scur)[QB]) {
+    constexpr int SJ = decltype(sj_tag)::value;
+    lds_barrier();
+    bf16x8 pb[QB][2];
+    float psum[QB];
+    Kn::probs(scur, scale_log2, st, pb, psum);
+#pragma unroll
+    for (int h = 0; h < QB; ++h) st[h].l += psum[h];
+    s16x8 va[2][NDB];
+    Kn::read_v(va, vst[SJ], v_row0, v_col);
+    Kn::pv_mfma(oacc, va, pb);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  int j = 0;
+  for (; j + 4 < kend; j += 4) {
+    iteration(I0{}, j, sa, sb);
+    iteration(I1{}, j + 1, sb, sa);
+    iteration(I2{}, j + 2, sa, sb);
+    iteration(I3{}, j + 3, sb, sa);
+  }
+  // 1..4 tiles remain (none if kend == 0); S(j) is in sa
+  const int rem = kend - j;
+  if (rem == 4) {
+    iteration(I0{}, j, sa, sb);
+    iteration(I1{}, j + 1, sb, sa);
+    iteration(I2{}, j + 2, sa, sb);
+    last(I3{}, sb);
+  } else if (rem == 3) {
+    iteration(I0{}, j, sa, sb);
+    iteration(I1{}, j + 1, sb, sa);
+    last(I2{}, sa);
+  } else if (rem == 2) {
+    iteration(I0{}, j, sa, sb);
+    last(I1{}, sb);
+  } else if (rem == 1) {
+    last(I0{}, sa);
   }
 
   // ---- epilogue: O = O^T / l, bf16, rows of this sequence only
-  if (wave_active) {
-    const float lt = half_swap_sum(l_run);
+#pragma unroll
+  for (int h = 0; h < QB; ++h) {
+    const float lt = half_swap_sum(st[h].l);
     const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (qrow < L) {
-      __bf16* orow = O + base + int64_t(qrow) * rs;
+    if (qrow[h] < L) {
+      __bf16* orow = O + base + int64_t(qrow[h]) * rs;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           bf16x4 w;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][4 * i4 + e] * inv);
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[h][db][4 * i4 + e] * inv);
           *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * i4 + 4 * g) = w;
         }
     }
@@ -233,16 +529,9 @@ int launch(const void* q, const void* k, const void* v, const int32_t* cu, const
   using Cfg = Bf16Cfg<D>;
   const int n = static_cast<int>(d->plan.items.size());
   if (n == 0) return PVA_OK;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_bf16_kernel<D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::SMEM) != hipSuccess)
-      return PVA_ERR_HIP;
-    attr_set = true;
-  }
   const float scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), Cfg::SMEM, stream,
-                     static_cast<const __bf16*>(q), static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu,
+  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, static_cast<const __bf16*>(q),
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu,
                      static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2,
                      static_cast<__bf16*>(out));
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;

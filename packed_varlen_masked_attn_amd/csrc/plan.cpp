@@ -23,7 +23,7 @@ namespace pva {
 TileShape tile_shape(pva_dtype dtype, int32_t head_dim) {
   (void)head_dim;
   if (dtype == PVA_FP8_E4M3) return TileShape{128, 64};
-  return TileShape{128, 64};
+  return TileShape{kBf16BlockM, kBf16BlockN};
 }
 
 namespace {

@@ -30,6 +30,14 @@ struct WorkItem {
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 
+// Tile shape of the bf16 kernel, shared with the planner (the work list's
+// key-tile indices are in units of kBf16BlockN keys).
+#ifndef PVA_BF16_BN
+#define PVA_BF16_BN 32
+#endif
+constexpr int32_t kBf16BlockM = 128;
+constexpr int32_t kBf16BlockN = PVA_BF16_BN;
+
 // Tile shape used by the kernels for a given element type and head size.
 struct TileShape {
   int32_t bm;  // query rows per work item
