@@ -46,16 +46,36 @@ namespace {
 
 template <int D>
 struct Bf16Cfg {
-  static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = 4, NT = 256;
   static constexpr int QB = PVA_BF16_QB;   // 32-row query blocks per wave
-  static_assert(BM == NW * QB * 32 && BN == 32, "4 waves x 64 query rows; 32-key tiles");
+  static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = BM / (32 * QB), NT = 64 * NW;
+  static_assert(BM == NW * QB * 32 && BN == 32, "waves x 32-row query blocks; 32-key tiles");
   static constexpr int C = D / 8;          // 16-byte chunks per K/V row
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
   static constexpr int TILE = BN * D * 2;  // bytes of one K or V tile
-  static constexpr int NLD = BN * C / NT;  // 16-byte DMA rounds per thread per tile and tensor
-  static_assert(NLD >= 1 && BN * C % NT == 0, "whole DMA rounds");
+  // 16-byte DMA rounds per wave per tile and tensor; when a tile has fewer
+  // chunks than the workgroup has lanes, only the first waves issue one
+  static constexpr int NLD = (BN * C + NT - 1) / NT;
+  static_assert((BN * C) % 64 == 0 && (BN * C >= NT ? (BN * C) % NT == 0 : true), "whole wave-sized DMA");
   static constexpr int NS = 4;             // LDS stages per tensor
+  // K rows are padded by one 16-byte chunk: the 16 consecutive rows a K
+  // operand read touches at one chunk then fall on 16 different bank groups,
+  // and the address stays affine in the chunk (one base register).
+  static constexpr int KROW = C + 1;                        // chunks per padded K row
+  static constexpr int KSLOTS = BN * KROW;                  // 16-byte slots of a K tile
+  static constexpr int KTILE = KSLOTS * 16;
+  static constexpr int NLDK = (KSLOTS + NT - 1) / NT;       // K DMA rounds (the last may be partial)
+  // V rows are padded by 64 bytes: the four consecutive rows a transpose read
+  // touches then sit in four different 64-byte quarters of the bank window,
+  // and the address stays affine in the column block (one base register).
+  static constexpr int VROW = C + 4;                        // chunks per padded V row
+  static constexpr int VSLOTS = BN * VROW;                  // 16-byte slots of a V tile
+  static constexpr int VTILE = VSLOTS * 16;
+  static constexpr int NLDV = (VSLOTS + NT - 1) / NT;       // V DMA rounds (the last may be partial)
+  // DMA instructions every wave issues per tile (some waves issue one more);
+  // the partial vmcnt waits count only these, so waves with more loads in
+  // flight simply wait a little longer
+  static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
 };
 
 // s_waitcnt with vmcnt = N and the other counters untouched (gfx9 encoding:
@@ -84,30 +104,66 @@ struct Kernel {
   static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-  // ---- global -> LDS (direct DMA). Lane writes 16 B at stage + 16 * slot;
-  // slot s holds row s / C, stored chunk s % C = global chunk (s % C) ^
-  // swizzle(row). Rows past the sequence end are clamped to its last row
-  // (finite data; the mask discards them).
-  template <bool IS_V>
-  static __device__ __forceinline__ void load_tile(const uint8_t* seq_base, int k0, int L, int64_t rs2,
-                                                   uint8_t* stage, int wave, int lane) {
+  // ---- global -> LDS (direct DMA) into a padded tile of ROW chunks per row.
+  // Lane writes 16 B at stage + 16 * slot; slot s holds row s / ROW, chunk
+  // s % ROW. Lanes that land on a pad chunk or past the tile are switched off
+  // (exec mask), so nothing is written there and nothing is fetched for them.
+  // Steady state: the tile base is a scalar and each lane adds a constant
+  // 32-bit offset (no per-load vector arithmetic). The last tile of a
+  // sequence clamps rows to the sequence end (finite data; the mask discards
+  // them).
+  template <int ROW, int SLOTS>
+  struct Loader {
+    static constexpr int ROUNDS = (SLOTS + Cfg::NT - 1) / Cfg::NT;
+    uint32_t off[ROUNDS];  // per-round lane offset within the tile (bytes)
+    int row[ROUNDS];       // per-round tile row of this lane
+    bool act[ROUNDS];      // lane holds a data chunk
+    __device__ __forceinline__ void init(int64_t rs2, int wave, int lane) {
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      const int s = Cfg::NT * i + 64 * wave + lane;
-      const int r = s / C, p = s % C;
-      const int c = p ^ (IS_V ? swz_v<C>(r) : swz_k<C>(r));
-      const int row = min(k0 + r, L - 1);
-      const uint8_t* src = seq_base + int64_t(row) * rs2 + 16 * c;
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (PVA_LDS void*)(stage + 16 * (Cfg::NT * i + 64 * wave)), 16, 0, 0);
+      for (int i = 0; i < ROUNDS; ++i) {
+        const int s = Cfg::NT * i + 64 * wave + lane;
+        const int r = s / ROW, p = s % ROW;
+        act[i] = s < SLOTS && p < C;
+        row[i] = r;
+        off[i] = act[i] ? uint32_t(r * rs2 + 16 * p) : 0u;
+      }
     }
-  }
+    __device__ __forceinline__ void load(const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
+                                         int wave, int lane) const {
+      if (k0 + BN <= L) {
+        const uint8_t* tile = seq_base + int64_t(k0) * rs2;  // scalar
+#pragma unroll
+        for (int i = 0; i < ROUNDS; ++i) {
+          const int s0 = Cfg::NT * i + 64 * wave;
+          if (s0 >= SLOTS) break;
+          if (act[i])
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + off[i]),
+                                             (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < ROUNDS; ++i) {
+          const int s0 = Cfg::NT * i + 64 * wave;
+          if (s0 >= SLOTS) break;
+          if (act[i]) {
+            const int s = s0 + lane, p = s % ROW;
+            const int rr = min(k0 + row[i], L - 1);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void*)(seq_base + int64_t(rr) * rs2 + 16 * p),
+                (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
+          }
+        }
+      }
+    }
+  };
+  using KLoader = Loader<Cfg::KROW, Cfg::KSLOTS>;
+  using VLoader = Loader<Cfg::VROW, Cfg::VSLOTS>;
 
-  // ---- K operands of one tile: row l32, chunk 2c + g (swizzled by row)
+  // ---- K operands of one tile: row l32, chunk 2c + g
   static __device__ __forceinline__ void read_k(bf16x8 (&a)[NKC], const uint8_t* kst, int l32, int g) {
 #pragma unroll
     for (int c = 0; c < NKC; ++c)
-      a[c] = *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * C + ((2 * c + g) ^ swz_k<C>(l32))));
+      a[c] = *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * Cfg::KROW + 2 * c + g));
   }
 
   // ---- V^T operands of one tile: for 16-key step kc and 32-column block db
@@ -115,16 +171,7 @@ struct Kernel {
 #pragma unroll
     for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + v_col;
-        const int chunk = col >> 3, boff = 2 * (col & 7);
-        const int r0 = 16 * kc + v_row0, r1 = r0 + 8;
-        const uint8_t* p0 = vst + 16 * (r0 * C + (chunk ^ swz_v<C>(r0))) + boff;
-        const uint8_t* p1 = vst + 16 * (r1 * C + (chunk ^ swz_v<C>(r1))) + boff;
-        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
-        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
-        a[kc][db] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      }
+      for (int db = 0; db < NDB; ++db) a[kc][db] = read_v_step(vst, kc * NDB + db, v_row0, v_col);
   }
 
   // ---- S^T = K Q^T for both query blocks (two independent MFMA chains)
@@ -194,19 +241,16 @@ struct Kernel {
                                                       float scale_log2, const RowState (&st)[QB],
                                                       bf16x8 (&pb)[QB][2], float (&psum)[QB], int l32, int g) {
     constexpr int PER_C = (QB * 16 + NKC - 1) / NKC;  // exponentials per d-chunk
-    const uint8_t* krow = kst + 16 * l32 * C;
-    const int sw = swz_k<C>(l32);
-    auto rd = [&](int c) { return *reinterpret_cast<const bf16x8*>(krow + 16 * ((2 * c + g) ^ sw)); };
+    const uint8_t* krow = kst + 16 * (l32 * Cfg::KROW + g);
+    auto rd = [&](int c) { return *reinterpret_cast<const bf16x8*>(krow + 32 * c); };
     bf16x8 ka[3];
     ka[0] = rd(0);
     if (NKC > 1) ka[1] = rd(1);
 #pragma unroll
     for (int h = 0; h < QB; ++h) snext[h] = f32x16{};
-    float part[QB][4];
+    float part[QB][2];
 #pragma unroll
-    for (int h = 0; h < QB; ++h)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) part[h][k] = 0.0f;
+    for (int h = 0; h < QB; ++h) part[h][0] = part[h][1] = 0.0f;
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
       if (c + 2 < NKC) ka[(c + 2) % 3] = rd(c + 2);
@@ -218,38 +262,45 @@ struct Kernel {
         const int idx = c * PER_C + e;  // element of the (QB x 16) probability tile
         if (idx < QB * 16) {
           const int h = idx / 16, i = idx % 16;
-          const float p = fast_exp2(fmaf(scur[h][i], scale_log2, -st[h].m));
-          part[h][i % 4] += p;
-          pb[h][i / 8][i % 8] = (__bf16)p;
+          pb[h][i / 8][i % 8] = (__bf16)fast_exp2(fmaf(scur[h][i], scale_log2, -st[h].m));
+          if (i % 2 == 1) {
+            // row sum of the bf16 probabilities PV actually uses, two at a time
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            const bf16x2 pair = {pb[h][i / 8][i % 8 - 1], pb[h][i / 8][i % 8]};
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            part[h][(i / 2) % 2] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[h][(i / 2) % 2], false);
+          }
         }
       }
     }
 #pragma unroll
-    for (int h = 0; h < QB; ++h) psum[h] = (part[h][0] + part[h][1]) + (part[h][2] + part[h][3]);
+    for (int h = 0; h < QB; ++h) psum[h] = part[h][0] + part[h][1];
     pin(pb, psum);
   }
 
   // ---- O^T += V^T P^T for both query blocks, interleaved in program order
   // with the row max of tile j+1: per (kc, db) step, one V^T operand read two
   // steps ahead, two MFMAs, then a few max operations.
+  static __device__ __forceinline__ s16x8 read_v_step(const uint8_t* vst, int step, int v_row0, int v_col) {
+    const int kc = step / NDB, db = step % NDB;
+    // rows 16 kc + v_row0 (+8), columns 32 db + v_col .. +3 of the padded tile
+    const uint8_t* p0 = vst + 16 * Cfg::VROW * (16 * kc + v_row0) + 2 * (32 * db + v_col);
+    const uint8_t* p1 = p0 + 16 * Cfg::VROW * 8;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
+    return s16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+
+  // `va0`, `va1`: the operands of steps 0 and 1, read early by the caller.
   static __device__ __forceinline__ void pv_with_max(f32x16 (&o)[QB][NDB], const uint8_t* vst,
                                                      const bf16x8 (&pb)[QB][2], const f32x16 (&snext)[QB],
-                                                     float scale_log2, float (&mt)[QB], int v_row0, int v_col) {
+                                                     float scale_log2, float (&mt)[QB], int v_row0, int v_col,
+                                                     s16x8 va0, s16x8 va1) {
     constexpr int NSTEP = 2 * NDB;
-    auto rd = [&](int step) {
-      const int kc = step / NDB, db = step % NDB;
-      const int col = 32 * db + v_col;
-      const int chunk = col >> 3, boff = 2 * (col & 7);
-      const int r0 = 16 * kc + v_row0, r1 = r0 + 8;
-      const uint8_t* p0 = vst + 16 * (r0 * C + (chunk ^ swz_v<C>(r0))) + boff;
-      const uint8_t* p1 = vst + 16 * (r1 * C + (chunk ^ swz_v<C>(r1))) + boff;
-      const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
-      const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
-      return s16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-    };
+    auto rd = [&](int step) { return read_v_step(vst, step, v_row0, v_col); };
     s16x8 va[3];
-    va[0] = rd(0);
-    va[1] = rd(1);
+    va[0] = va0;
+    va[1] = va1;
     float mx[QB];
 #pragma unroll
     for (int h = 0; h < QB; ++h) mx[h] = snext[h][0];
@@ -302,20 +353,23 @@ struct Kernel {
                                                bf16x8 (&pb)[QB][2], float (&psum)[QB]) {
 #pragma unroll
     for (int h = 0; h < QB; ++h) {
-      float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // short dependency chains
+      float part[2] = {0.0f, 0.0f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(s[h][i], scale_log2, -st[h].m));
-        part[i % 4] += p;
-        pb[h][i / 8][i % 8] = (__bf16)p;
+      for (int i = 0; i < 16; ++i) pb[h][i / 8][i % 8] = (__bf16)fast_exp2(fmaf(s[h][i], scale_log2, -st[h].m));
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        const bf16x2 pair = {pb[h][i / 8][i % 8], pb[h][i / 8][i % 8 + 1]};
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        part[(i / 2) % 2] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[(i / 2) % 2], false);
       }
-      psum[h] = (part[0] + part[1]) + (part[2] + part[3]);
+      psum[h] = part[0] + part[1];
     }
   }
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
+__global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
                                                           const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V,
                                                           const int32_t* __restrict__ cu,
@@ -328,8 +382,8 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
   static_assert(NS == 4, "the loop below is unrolled for a ring of four stages");
   // separate arrays per stage: the compiler sees that an LDS DMA into one
   // stage and reads of another do not alias
-  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::TILE], k1s[Cfg::TILE], k2s[Cfg::TILE], k3s[Cfg::TILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::TILE], v1s[Cfg::TILE], v2s[Cfg::TILE], v3s[Cfg::TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::KTILE], k1s[Cfg::KTILE], k2s[Cfg::KTILE], k3s[Cfg::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::VTILE], v1s[Cfg::VTILE], v2s[Cfg::VTILE], v3s[Cfg::VTILE];
   uint8_t* const kst[NS] = {k0s, k1s, k2s, k3s};
   uint8_t* const vst[NS] = {v0s, v1s, v2s, v3s};
 
@@ -362,8 +416,12 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
   const int kend = it.k_end;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
-  auto ld_k = [&](int t, uint8_t* stage) { Kn::template load_tile<false>(Kb, t * BN, L, rs2, stage, wave, lane); };
-  auto ld_v = [&](int t, uint8_t* stage) { Kn::template load_tile<true>(Vb, t * BN, L, rs2, stage, wave, lane); };
+  typename Kn::KLoader kld;
+  typename Kn::VLoader vld;
+  kld.init(rs2, wave, lane);
+  vld.init(rs2, wave, lane);
+  auto ld_k = [&](int t, uint8_t* stage) { kld.load(Kb, t * BN, L, rs2, stage, wave, lane); };
+  auto ld_v = [&](int t, uint8_t* stage) { vld.load(Vb, t * BN, L, rs2, stage, wave, lane); };
   if (kend > 0) ld_k(0, kst[0]);
   if (kend > 1) ld_k(1, kst[1]);
   if (kend > 0) ld_v(0, vst[0]);
@@ -399,7 +457,7 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
 
   // K0, K1, V0 must have landed; K2 V1 K3 V2 may still be in flight
   if (kend > 3)
-    wait_vmcnt<4 * NLD>();
+    wait_vmcnt<2 * Cfg::DMA_MIN>();
   else
     wait_vmcnt<0>();
   lds_barrier();
@@ -420,7 +478,9 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
   }
 
   // Steady-state iteration j (j + 1 < kend); `scur` holds S(j), `snext`
-  // receives S(j+1). SJ = j % NS (compile-time in each unrolled copy).
+  // receives S(j+1). SJ = j % NS (compile-time in each unrolled copy). The
+  // rare branches (element mask, rescale) are marked unlikely so that the
+  // common path falls through without a taken branch.
   auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[QB], f32x16(&snext)[QB]) {
     constexpr int SJ = decltype(sj_tag)::value;
     lds_barrier();  // every wave is done with S(j) (K stage SJ) and PV(j-1) (V stage SJ-1)
@@ -428,20 +488,23 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
     if (steady) ld_k(j + NS, kst[SJ]);
     if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
     const int k1 = (j + 1) * BN;
+    // the first two V^T operands of PV(j): their LDS latency hides behind block A
+    const s16x8 va0 = Kn::read_v_step(vst[SJ], 0, v_row0, v_col);
+    const s16x8 va1 = Kn::read_v_step(vst[SJ], 1, v_row0, v_col);
     // S(j+1) MFMAs interleaved with the exponentials of tile j
     bf16x8 pb[QB][2];
     float psum[QB];
     Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st, pb, psum, l32, g);
 #pragma unroll
     for (int h = 0; h < QB; ++h) st[h].l += psum[h];
-    if (k1 + BN > wlim_min) Kn::mask(snext, k1, g, mylim);
+    if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs interleaved with the row max of tile j+1
     float mt[QB];
-    Kn::pv_with_max(oacc, vst[SJ], pb, snext, scale_log2, mt, v_row0, v_col);
+    Kn::pv_with_max(oacc, vst[SJ], pb, snext, scale_log2, mt, v_row0, v_col, va0, va1);
 #pragma unroll
     for (int h = 0; h < QB; ++h) {
       const bool need = mt[h] > st[h].m + kLazyRescale;
-      if (wave_any(need)) {
+      if (__builtin_expect(wave_any(need), 0)) {
         // per-lane decision: a lane that does not need it keeps its max (alpha = 1
         // exactly), so each row's arithmetic depends on its own scores only
         const float alpha = need ? fast_exp2(st[h].m - mt[h]) : 1.0f;
@@ -454,9 +517,9 @@ __global__ __launch_bounds__(256, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __
       }
     }
     // K(j+2) and V(j+1) are needed next; the loads of iterations j-1 and j
-    // (2 tiles x 2 tensors x NLD each) may stay in flight in steady state
+    // may stay in flight in steady state
     if (steady)
-      wait_vmcnt<4 * NLD>();
+      wait_vmcnt<2 * Cfg::DMA_MIN>();
     else
       wait_vmcnt<0>();
   };

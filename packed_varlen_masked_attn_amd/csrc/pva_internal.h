@@ -35,7 +35,10 @@ static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 #ifndef PVA_BF16_BN
 #define PVA_BF16_BN 32
 #endif
-constexpr int32_t kBf16BlockM = 128;
+#ifndef PVA_BF16_BM
+#define PVA_BF16_BM 128
+#endif
+constexpr int32_t kBf16BlockM = PVA_BF16_BM;
 constexpr int32_t kBf16BlockN = PVA_BF16_BN;
 
 // Tile shape used by the kernels for a given element type and head size.
