@@ -78,86 +78,15 @@ struct Bf16Cfg {
   static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
 };
 
-// s_waitcnt with vmcnt = N and the other counters untouched (gfx9 encoding:
-// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-// Workgroup barrier without the global-memory fence __syncthreads() implies
-// (that fence would also wait for every DMA still in flight). LDS reads issued
-// before it have been consumed by then; the memory clobber keeps the
-// compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-// Per-lane state of the online softmax for one query column.
-struct RowState {
-  float m;  // reference max (log2 units); O and l are relative to it
-  float l;  // this lane's partial row sum (the other half-wave holds the rest)
-};
-
 template <int D>
 struct Kernel {
   using Cfg = Bf16Cfg<D>;
   static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-  // ---- global -> LDS (direct DMA) into a padded tile of ROW chunks per row.
-  // Lane writes 16 B at stage + 16 * slot; slot s holds row s / ROW, chunk
-  // s % ROW. Lanes that land on a pad chunk or past the tile are switched off
-  // (exec mask), so nothing is written there and nothing is fetched for them.
-  // Steady state: the tile base is a scalar and each lane adds a constant
-  // 32-bit offset (no per-load vector arithmetic). The last tile of a
-  // sequence clamps rows to the sequence end (finite data; the mask discards
-  // them).
-  template <int ROW, int SLOTS>
-  struct Loader {
-    static constexpr int ROUNDS = (SLOTS + Cfg::NT - 1) / Cfg::NT;
-    uint32_t off[ROUNDS];  // per-round lane offset within the tile (bytes)
-    int row[ROUNDS];       // per-round tile row of this lane
-    bool act[ROUNDS];      // lane holds a data chunk
-    __device__ __forceinline__ void init(int64_t rs2, int wave, int lane) {
-#pragma unroll
-      for (int i = 0; i < ROUNDS; ++i) {
-        const int s = Cfg::NT * i + 64 * wave + lane;
-        const int r = s / ROW, p = s % ROW;
-        act[i] = s < SLOTS && p < C;
-        row[i] = r;
-        off[i] = act[i] ? uint32_t(r * rs2 + 16 * p) : 0u;
-      }
-    }
-    __device__ __forceinline__ void load(const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
-                                         int wave, int lane) const {
-      if (k0 + BN <= L) {
-        const uint8_t* tile = seq_base + int64_t(k0) * rs2;  // scalar
-#pragma unroll
-        for (int i = 0; i < ROUNDS; ++i) {
-          const int s0 = Cfg::NT * i + 64 * wave;
-          if (s0 >= SLOTS) break;
-          if (act[i])
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(tile + off[i]),
-                                             (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < ROUNDS; ++i) {
-          const int s0 = Cfg::NT * i + 64 * wave;
-          if (s0 >= SLOTS) break;
-          if (act[i]) {
-            const int s = s0 + lane, p = s % ROW;
-            const int rr = min(k0 + row[i], L - 1);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void*)(seq_base + int64_t(rr) * rs2 + 16 * p),
-                (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
-          }
-        }
-      }
-    }
-  };
-  using KLoader = Loader<Cfg::KROW, Cfg::KSLOTS>;
-  using VLoader = Loader<Cfg::VROW, Cfg::VSLOTS>;
+  // ---- K and V tiles: rows padded to KROW / VROW 16-byte slots
+  using KLoader = DmaLoader<Cfg::NT, BN, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
+  using VLoader = DmaLoader<Cfg::NT, BN, Cfg::VROW, Cfg::VSLOTS, PaddedRows<C>>;
 
   // ---- K operands of one tile: row l32, chunk 2c + g
   static __device__ __forceinline__ void read_k(bf16x8 (&a)[NKC], const uint8_t* kst, int l32, int g) {
@@ -477,7 +406,7 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
     for (int h = 0; h < QB; ++h) st[h].m = mt[h];  // first tile: O and l are still zero
   }
 
-  // Steady-state iteration j (j + 1 < kend); `scur` holds S(j), `snext`
+  // Iteration j; `scur` holds S(j), `snext`
   // receives S(j+1). SJ = j % NS (compile-time in each unrolled copy). The
   // rare branches (element mask, rescale) are marked unlikely so that the
   // common path falls through without a taken branch.
@@ -523,47 +452,22 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
     else
       wait_vmcnt<0>();
   };
-  // Last iteration: probabilities and PV of the final tile only.
-  auto last = [&](auto sj_tag, f32x16(&scur)[QB]) {
-    constexpr int SJ = decltype(sj_tag)::value;
-    lds_barrier();
-    bf16x8 pb[QB][2];
-    float psum[QB];
-    Kn::probs(scur, scale_log2, st, pb, psum);
-#pragma unroll
-    for (int h = 0; h < QB; ++h) st[h].l += psum[h];
-    s16x8 va[2][NDB];
-    Kn::read_v(va, vst[SJ], v_row0, v_col);
-    Kn::pv_mfma(oacc, va, pb);
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
   using I3 = std::integral_constant<int, 3>;
 
-  int j = 0;
-  for (; j + 4 < kend; j += 4) {
+  // Four unrolled iterations per trip, each guarded; the last tile's
+  // iteration also computes S of the tile after it on a stale stage, which
+  // the mask turns entirely into -inf (no effect on the result).
+  for (int j = 0; j < kend; j += 4) {
     iteration(I0{}, j, sa, sb);
+    if (j + 1 >= kend) break;
     iteration(I1{}, j + 1, sb, sa);
+    if (j + 2 >= kend) break;
     iteration(I2{}, j + 2, sa, sb);
+    if (j + 3 >= kend) break;
     iteration(I3{}, j + 3, sb, sa);
-  }
-  // 1..4 tiles remain (none if kend == 0); S(j) is in sa
-  const int rem = kend - j;
-  if (rem == 4) {
-    iteration(I0{}, j, sa, sb);
-    iteration(I1{}, j + 1, sb, sa);
-    iteration(I2{}, j + 2, sa, sb);
-    last(I3{}, sb);
-  } else if (rem == 3) {
-    iteration(I0{}, j, sa, sb);
-    iteration(I1{}, j + 1, sb, sa);
-    last(I2{}, sa);
-  } else if (rem == 2) {
-    iteration(I0{}, j, sa, sb);
-    last(I1{}, sb);
-  } else if (rem == 1) {
-    last(I0{}, sa);
   }
 
   // ---- epilogue: O = O^T / l, bf16, rows of this sequence only

@@ -1,11 +1,404 @@
-// FP8 (OCP E4M3FN) variant of the packed mixed-mask attention forward.
+// FP8 (OCP E4M3FN) packed mixed-mask attention forward for gfx950; bf16 out.
+//
+// Same operation and mask as the bf16 kernel ("[RFC]: HunyuanImage 3.0
+// deployment", Proposed Change P0 and Model structure item 1). Q, K and V are
+// E4M3 codes with one fp32 dequantisation scale per (sequence, head) and
+// tensor; QK^T and PV run on the fp8 MFMA (v_mfma_f32_32x32x64_f8f6f4, twice
+// the bf16 rate), with fp32 accumulation.
+//
+// One workgroup = 4 waves = one work item (sequence, head, 128 query rows);
+// each wave owns 32 query rows. Keys are streamed in tiles of 64, so that one
+// lane's 32 probabilities of a tile form exactly one K=64 MFMA operand.
+//
+// Per wave and key tile j:
+//   S^T[key, q] = K Q^T     two 32-key blocks x two 64-wide steps over d;
+//                           A = K from LDS (32 contiguous bytes per lane),
+//                           B = Q^T in registers for the whole item.
+//   softmax in fp32, log2 domain, with the score scale q_s * k_s * scale
+//   folded into the exponent; lazy rescaling as in the bf16 kernel.
+//   P is quantised to E4M3 (round to nearest even) straight from the S^T
+//   accumulators into the B operand of PV; probabilities stay <= 2^8, well
+//   inside the format's range.
+//   O^T[d, q] += V^T P^T    A = V^T read with ds_read_b64_tr_b8 (8 keys of
+//                           one column per read); a fifth 32-row block whose A
+//                           operand is all ones accumulates l = sum of the
+//                           quantised probabilities, i.e. exactly the weights
+//                           PV applied, so every output row is a convex
+//                           combination of V rows (this keeps early causal
+//                           text rows, which have few keys, accurate).
+//   O = O^T * v_s / l at the end.
+// The software pipeline (LDS DMA rings, S(j+1) MFMAs beside the exponentials
+// of tile j, PV(j) MFMAs beside the row max of tile j+1) is the bf16
+// kernel's.
+#include <type_traits>
+
 #include "kernel_common.h"
 
 namespace pva {
 
-int launch_fwd_fp8(const void*, const void*, const void*, const float*, const float*, const float*,
-                   const int32_t*, const pva_seg_desc*, float, void*, hipStream_t) {
-  return PVA_ERR_UNSUPPORTED;
+namespace {
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+struct Fp8Cfg {
+  static constexpr int D = 128;
+  static constexpr int BM = 128, BN = 64, NW = 4, NT = 256;
+  static constexpr int NB = BN / 32;   // 32-key blocks per tile
+  static constexpr int C = D / 16;     // 16-byte chunks per K/V row
+  static constexpr int NKS = D / 64;   // 64-wide MFMA steps over d for S^T
+  static constexpr int NDB = D / 32;   // 32-row blocks of O^T (plus one block for l)
+  static constexpr int NS = 4;         // LDS stages per tensor
+  // K rows padded by one chunk (conflict-free 16-byte operand reads, affine
+  // addresses); V rows unpadded with XOR-swizzled 32-byte pairs
+  static constexpr int KROW = C + 1, KSLOTS = BN * KROW, KTILE = KSLOTS * 16;
+  static constexpr int VROW = C, VSLOTS = BN * VROW, VTILE = VSLOTS * 16;
+  static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
+};
+
+// Position of a V row's 32-byte column pairs: pair p of row k sits at pair
+// p ^ vswz(k). A transpose read touches, for one half-wave, the rows
+// {0,1,2,3,8,9,10,11} + 16 r + 4 g of the tile at one pair; with this
+// swizzle the same-parity rows among them land on four different pairs, so
+// the eight rows fill the 256-byte bank window once.
+__device__ __forceinline__ int vswz(int k) { return ((k >> 1) + ((k >> 3) << 1)) & 3; }
+
+struct VSwizzledPairs {
+  static __device__ __forceinline__ int chunk(int row, int pos) {
+    return 2 * ((pos >> 1) ^ vswz(row)) + (pos & 1);
+  }
+};
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  // E4M3 x E4M3 (format code 0 for both operands), no block scales
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+struct Fp8Kernel {
+  using Cfg = Fp8Cfg;
+  static constexpr int BN = Cfg::BN, NB = Cfg::NB, C = Cfg::C, NKS = Cfg::NKS, NDB = Cfg::NDB;
+  using KLoader = DmaLoader<Cfg::NT, BN, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
+  using VLoader = DmaLoader<Cfg::NT, BN, Cfg::VROW, Cfg::VSLOTS, VSwizzledPairs>;
+
+  // K operand of 64-wide step c for key block b: row 32 b + l32, bytes
+  // 64 c + 32 g .. +31 (any d assignment works as long as Q uses the same)
+  static __device__ __forceinline__ i32x8 read_k(const uint8_t* kst, int b, int c, int l32, int g) {
+    return *reinterpret_cast<const i32x8*>(kst + 16 * Cfg::KROW * (32 * b + l32) + 64 * c + 32 * g);
+  }
+
+  // V^T operand of column block db: byte 8 r + e of lane l is
+  // V[16 r + 8 (e / 4) + 4 g + e % 4][32 db + l % 32], the same key order as
+  // the probability operand: its byte j = 16 b + i holds element (b, i) of
+  // the S^T accumulators, key 32 b + 8 (i / 4) + 4 g + i % 4.
+  static __device__ __forceinline__ i32x8 read_v(const uint8_t* vst, int db, const int (&vrow0)[1], int vsw,
+                                                 int half, int p8) {
+    i32x8 a;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint8_t* src = vst + 16 * Cfg::VROW * (16 * r + vrow0[0]) + 32 * (db ^ vsw) + 16 * half + p8;
+      const i32x2 t = __builtin_amdgcn_ds_read_tr8_b64_v2i32((PVA_LDS i32x2*)(src));
+      a[2 * r] = t[0];
+      a[2 * r + 1] = t[1];
+    }
+    return a;
+  }
+
+  static __device__ __forceinline__ void mask(f32x16 (&s)[NB], int k0, int g, int mylim) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * b + 8 * (i / 4) + 4 * g + (i % 4);
+        if (key >= mylim) s[b][i] = -INFINITY;
+      }
+  }
+
+  static __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB], float scale_log2) {
+    float mx = s[0][0];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+    return half_swap_max(mx) * scale_log2;
+  }
+
+  // E4M3 probabilities of one element pair -> two bytes of a packed dword
+  // (HI selects the upper 16 bits; the other half of `old` is kept)
+  template <bool HI>
+  static __device__ __forceinline__ int pack2(float a, float b, int old) {
+    return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+  }
+
+  // S(j+1) MFMAs, one K operand read ahead, each followed by a quarter of
+  // the probabilities of tile j (program-order interleave, bounded registers)
+  static __device__ __forceinline__ void s_with_probs(f32x16 (&snext)[NB], const uint8_t* kst,
+                                                      const i32x8 (&qf)[NKS], const f32x16 (&scur)[NB],
+                                                      float scale_log2, float m, i32x8& pb, int l32, int g) {
+    constexpr int NSTEP = NB * NKS;  // (b, c) pairs
+    constexpr int WPS = 8 / NSTEP;   // packed probability dwords per MFMA step
+    i32x8 ka = read_k(kst, 0, 0, l32, g);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) snext[b] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      const int c = st / NB, b = st % NB;
+      i32x8 kn;
+      if (st + 1 < NSTEP) kn = read_k(kst, (st + 1) % NB, (st + 1) / NB, l32, g);
+      snext[b] = mfma_fp8(ka, qf[c], snext[b]);
+#pragma unroll
+      for (int ww = 0; ww < WPS; ++ww) {
+        const int w = st * WPS + ww, pbb = w / 4, i0 = 4 * (w % 4);
+        const float p0 = fast_exp2(fmaf(scur[pbb][i0 + 0], scale_log2, -m));
+        const float p1 = fast_exp2(fmaf(scur[pbb][i0 + 1], scale_log2, -m));
+        const float p2 = fast_exp2(fmaf(scur[pbb][i0 + 2], scale_log2, -m));
+        const float p3 = fast_exp2(fmaf(scur[pbb][i0 + 3], scale_log2, -m));
+        pb[w] = pack2<true>(p2, p3, pack2<false>(p0, p1, 0));
+      }
+      if (st + 1 < NSTEP) ka = kn;
+    }
+    pin(pb);
+  }
+
+  // PV(j) MFMAs (NDB column blocks + the ones block), one V^T operand read
+  // ahead, each followed by a slice of the row max of tile j+1
+  static __device__ __forceinline__ float pv_with_max(f32x16 (&o)[NDB + 1], const uint8_t* vst, const i32x8& pb,
+                                                      const i32x8& ones, const f32x16 (&snext)[NB],
+                                                      float scale_log2, const int (&vrow0)[1], int vsw, int half,
+                                                      int p8) {
+    constexpr int PER = (NB * 16 + NDB - 1) / NDB;  // max operations per PV step
+    float mx = snext[0][0];
+    i32x8 va = read_v(vst, 0, vrow0, vsw, half, p8);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      i32x8 vn;
+      if (db + 1 < NDB) vn = read_v(vst, db + 1, vrow0, vsw, half, p8);
+      o[db] = mfma_fp8(va, pb, o[db]);
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int idx = db * PER + e;
+        if (idx < NB * 16) mx = fmaxf(mx, snext[idx / 16][idx % 16]);
+      }
+      if (db + 1 < NDB) va = vn;
+    }
+    o[NDB] = mfma_fp8(ones, pb, o[NDB]);
+    return half_swap_max(mx) * scale_log2;
+  }
+
+  // second PV pass with the E4M3 residuals of a tile's probabilities
+  static __device__ __forceinline__ void pv_residual(f32x16 (&o)[NDB + 1], const uint8_t* vst,
+                                                     const f32x16 (&s)[NB], float scale_log2, float m,
+                                                     const i32x8& pb, const i32x8& ones, const int (&vrow0)[1],
+                                                     int vsw, int half, int p8) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    i32x8 pl;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int b = w / 4, i0 = 4 * (w % 4);
+      const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], false);
+      const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], true);
+      const float p0 = fast_exp2(fmaf(s[b][i0 + 0], scale_log2, -m)) - h01[0];
+      const float p1 = fast_exp2(fmaf(s[b][i0 + 1], scale_log2, -m)) - h01[1];
+      const float p2 = fast_exp2(fmaf(s[b][i0 + 2], scale_log2, -m)) - h23[0];
+      const float p3 = fast_exp2(fmaf(s[b][i0 + 3], scale_log2, -m)) - h23[1];
+      pl[w] = pack2<true>(p2, p3, pack2<false>(p0, p1, 0));
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8(read_v(vst, db, vrow0, vsw, half, p8), pl, o[db]);
+    o[NDB] = mfma_fp8(ones, pl, o[NDB]);
+  }
+
+  static __device__ __forceinline__ void pin(i32x8& pb) {
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      int v = pb[w];
+      asm volatile("" : "+v"(v));
+      pb[w] = v;
+    }
+  }
+};
+
+__global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K,
+                                                         const uint8_t* __restrict__ V,
+                                                         const float* __restrict__ q_scale,
+                                                         const float* __restrict__ k_scale,
+                                                         const float* __restrict__ v_scale,
+                                                         const int32_t* __restrict__ cu,
+                                                         const WorkItem* __restrict__ items, int H,
+                                                         float scale_log2e, __bf16* __restrict__ O) {
+  using Kn = Fp8Kernel;
+  using Cfg = Fp8Cfg;
+  constexpr int D = Cfg::D, BN = Cfg::BN, NB = Cfg::NB, NKS = Cfg::NKS, NDB = Cfg::NDB, NS = Cfg::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::KTILE], k1s[Cfg::KTILE], k2s[Cfg::KTILE], k3s[Cfg::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::VTILE], v1s[Cfg::VTILE], v2s[Cfg::VTILE], v3s[Cfg::VTILE];
+  uint8_t* const kst[NS] = {k0s, k1s, k2s, k3s};
+  uint8_t* const vst[NS] = {v0s, v1s, v2s, v3s};
+
+  const WorkItem it = items[blockIdx.x];
+  if (it.seq < 0) return;  // empty slot; uniform over the workgroup
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
+  const int T = it.text_len, L = it.seq_len;
+  const int64_t rs = int64_t(H) * D;  // bytes (one byte per element) between tokens of one head
+  const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
+  const uint8_t* Qh = Q + base;
+  const uint8_t* Kb = K + base;
+  const uint8_t* Vb = V + base;
+  const int sh = it.seq * H + it.head;
+  const float scale_log2 = q_scale[sh] * k_scale[sh] * scale_log2e;  // log2 units per raw score
+  const float vs = v_scale[sh];
+
+  const int qrow = it.q0 + 32 * wave + l32;
+  const int mylim = key_limit(qrow, T, L);
+  const int wrow0 = it.q0 + 32 * wave;
+  const bool wave_active = wrow0 < L;
+  const int wlim_min = key_limit(wrow0, T, L);
+  const int kend = it.k_end;
+
+  typename Kn::KLoader kld;
+  typename Kn::VLoader vld;
+  kld.init(rs, wave, lane);
+  vld.init(rs, wave, lane);
+  auto ld_k = [&](int t, uint8_t* stage) { kld.load(Kb, t * BN, L, rs, stage, wave, lane); };
+  auto ld_v = [&](int t, uint8_t* stage) { vld.load(Vb, t * BN, L, rs, stage, wave, lane); };
+  if (kend > 0) ld_k(0, kst[0]);
+  if (kend > 1) ld_k(1, kst[1]);
+  if (kend > 0) ld_v(0, vst[0]);
+  if (kend > 2) ld_k(2, kst[2]);
+  if (kend > 1) ld_v(1, vst[1]);
+  if (kend > 3) ld_k(3, kst[3]);
+  if (kend > 2) ld_v(2, vst[2]);
+
+  // Q^T operands: step c holds d = 64 c + 32 g .. +31 of this lane's query row
+  i32x8 qf[NKS];
+#pragma unroll
+  for (int c = 0; c < NKS; ++c) {
+    if (qrow < L)
+      qf[c] = *reinterpret_cast<const i32x8*>(Qh + int64_t(qrow) * rs + 64 * c + 32 * g);
+    else
+      qf[c] = i32x8{};
+  }
+
+  // O^T accumulators; block NDB accumulates l (ones operand)
+  f32x16 oacc[NDB + 1];
+#pragma unroll
+  for (int db = 0; db <= NDB; ++db) oacc[db] = f32x16{};
+  i32x8 ones;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;  // E4M3 1.0 in every byte
+  float m_run = -INFINITY;
+
+  // per-lane constant parts of the V^T transpose-read addresses: this lane
+  // feeds key row 16 r + vrow0 (r = 0..3), columns 32 db + 16 half + 8 p8
+  const int e = (lane & 15) >> 1;
+  const int vrow0[1] = {8 * (e >> 2) + 4 * g + (e & 3)};
+  const int vsw = vswz(vrow0[0]);
+  const int half = (lane >> 4) & 1, p8 = 8 * (lane & 1);
+
+  if (kend > 3)
+    wait_vmcnt<2 * Cfg::DMA_MIN>();
+  else
+    wait_vmcnt<0>();
+  lds_barrier();
+
+  auto s_mfma = [&](f32x16(&s)[NB], const uint8_t* kt) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) s[b] = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NKS; ++c)
+#pragma unroll
+      for (int b = 0; b < NB; ++b) s[b] = mfma_fp8(Kn::read_k(kt, b, c, l32, g), qf[c], s[b]);
+  };
+
+  f32x16 sa[NB], sb[NB];
+  if (kend > 0) {
+    s_mfma(sa, kst[0]);
+    if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
+    m_run = Kn::tile_max(sa, scale_log2);
+  }
+
+  auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[NB], f32x16(&snext)[NB]) {
+    constexpr int SJ = decltype(sj_tag)::value;
+    lds_barrier();
+    const bool steady = j + NS < kend;
+    if (steady) ld_k(j + NS, kst[SJ]);
+    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
+    const int k1 = (j + 1) * BN;
+    // S(j+1) MFMAs beside the exponentials of tile j
+    i32x8 pb;
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run, pb, l32, g);
+    if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
+    // PV(j) MFMAs beside the row max of tile j+1
+    const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, scale_log2, vrow0, vsw, half, p8);
+    // A tile the mask cuts for this wave (where rows with few keys live, e.g.
+    // early causal text rows) also gets the E4M3 residual of each probability,
+    // lo = q(p - hi), through a second PV pass: hi + lo carries p to about
+    // 2^-8 relative instead of 2^-4. S(j) is still live here.
+    if (__builtin_expect(k1 > wlim_min, 0))
+      Kn::pv_residual(oacc, vst[SJ], scur, scale_log2, m_run, pb, ones, vrow0, vsw, half, p8);
+    const bool need = mt > m_run + kLazyRescale;
+    if (__builtin_expect(wave_any(need), 0)) {
+      const float alpha = need ? fast_exp2(m_run - mt) : 1.0f;
+#pragma unroll
+      for (int db = 0; db <= NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      m_run = need ? mt : m_run;
+    }
+    if (steady)
+      wait_vmcnt<2 * Cfg::DMA_MIN>();
+    else
+      wait_vmcnt<0>();
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Four unrolled iterations per trip, each guarded; the last tile's
+  // iteration also computes S of the tile after it on a stale stage, which
+  // the mask turns entirely into -inf (no effect on the result).
+  for (int j = 0; j < kend; j += 4) {
+    iteration(I0{}, j, sa, sb);
+    if (j + 1 >= kend) break;
+    iteration(I1{}, j + 1, sb, sa);
+    if (j + 2 >= kend) break;
+    iteration(I2{}, j + 2, sa, sb);
+    if (j + 3 >= kend) break;
+    iteration(I3{}, j + 3, sb, sa);
+  }
+
+  // ---- epilogue: O = O^T * v_s / l (l from the ones block), bf16
+  if (wave_active && qrow < L) {
+    const float lt = oacc[NDB][0];
+    const float inv = lt > 0.0f ? vs / lt : 0.0f;
+    __bf16* orow = O + (int64_t(cu[it.seq]) + qrow) * H * D + int64_t(it.head) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) w[e2] = (__bf16)(oacc[db][4 * i4 + e2] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * i4 + 4 * g) = w;
+      }
+  }
+}
+
+}  // namespace
+
+int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks, const float* vs,
+                   const int32_t* cu, const pva_seg_desc* d, float scale, void* out, hipStream_t stream) {
+  if (d->plan.head_dim != Fp8Cfg::D) return PVA_ERR_UNSUPPORTED;
+  if (d->plan.tile.bm != Fp8Cfg::BM || d->plan.tile.bn != Fp8Cfg::BN) return PVA_ERR_UNSUPPORTED;
+  const int n = static_cast<int>(d->plan.items.size());
+  if (n == 0) return PVA_OK;
+  const float scale_log2e = static_cast<float>(double(scale) * 1.4426950408889634);
+  hipLaunchKernelGGL(fwd_fp8_kernel, dim3(n), dim3(Fp8Cfg::NT), 0, stream, static_cast<const uint8_t*>(q),
+                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), qs, ks, vs, cu,
+                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2e,
+                     static_cast<__bf16*>(out));
+  return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;
 }
 
 }  // namespace pva

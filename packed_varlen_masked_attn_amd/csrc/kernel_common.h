@@ -55,4 +55,79 @@ __device__ __forceinline__ bool wave_any(bool p) { return __builtin_amdgcn_ballo
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt with vmcnt = N and the other counters untouched (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt 7, lgkmcnt 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier without the global-memory fence __syncthreads() implies
+// (that fence would also wait for every DMA still in flight). LDS reads issued
+// before it have been consumed by then; the memory clobber keeps the
+// compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Per-lane state of the online softmax for one query column.
+struct RowState {
+  float m;  // reference max (log2 units); O and l are relative to it
+  float l;  // this lane's partial row sum (the other half-wave holds the rest)
+};
+
+// Direct global -> LDS DMA of one key tile (BN rows of a K or V head slice)
+// into a tile of ROW 16-byte slots per row (SLOTS slots in all). Lane writes
+// 16 B at stage + 16 * slot; slot s holds tile row s / ROW at slot position
+// s % ROW, which Map::chunk(row, pos) maps to the global 16-byte chunk it
+// carries, or to -1 for a pad slot. Lanes on pad slots or past the tile are
+// switched off, so nothing is fetched or written for them. In steady state
+// the tile base is a scalar and each lane adds a constant 32-bit offset; the
+// last tile of a sequence clamps rows to the sequence end (finite data that
+// the mask discards).
+template <int NT, int BN, int ROW, int SLOTS, typename Map>
+struct DmaLoader {
+  static constexpr int ROUNDS = (SLOTS + NT - 1) / NT;
+  uint32_t off[ROUNDS];  // per-round lane offset within the tile (bytes)
+  bool act[ROUNDS];      // lane carries data
+  __device__ __forceinline__ void init(int64_t rs2, int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int s = NT * i + 64 * wave + lane;
+      const int r = s / ROW, c = Map::chunk(r, s % ROW);
+      act[i] = s < SLOTS && c >= 0;
+      off[i] = act[i] ? uint32_t(r * rs2 + 16 * c) : 0u;
+    }
+  }
+  // one round (a no-op for waves whose round starts past the tile)
+  __device__ __forceinline__ void round(int i, const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
+                                        int wave, int lane) const {
+    const int s0 = NT * i + 64 * wave;
+    if (s0 >= SLOTS) return;
+    if (!act[i]) return;
+    const uint8_t* src;
+    if (k0 + BN <= L) {
+      src = seq_base + int64_t(k0) * rs2 + off[i];
+    } else {
+      const int s = s0 + lane, r = s / ROW;
+      src = seq_base + int64_t(min(k0 + r, L - 1)) * rs2 + 16 * Map::chunk(r, s % ROW);
+    }
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
+  }
+  __device__ __forceinline__ void load(const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
+                                       int wave, int lane) const {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) round(i, seq_base, k0, L, rs2, stage, wave, lane);
+  }
+  // DMA instructions every wave issues per tile (some waves issue one more)
+  static constexpr int MIN_PER_WAVE = SLOTS / NT;
+};
+
+// Row-padded layout: the first CHUNKS slots of a row are the row's chunks in
+// order, the rest are pad.
+template <int CHUNKS>
+struct PaddedRows {
+  static __device__ __forceinline__ int chunk(int, int pos) { return pos < CHUNKS ? pos : -1; }
+};
+
 }  // namespace pva

@@ -64,3 +64,22 @@ def sample_rows(T: int, L: int, rng: np.random.Generator, n_random: int = 24) ->
         cand.add((L // 128) * 128 + (b % 3))
     cand.update(int(x) for x in rng.integers(0, L, size=n_random))
     return sorted(r for r in cand if 0 <= r < L)
+
+
+def run_fp8(w: workloads.Workload, scale=None, stream=None):
+    """fp8 path: returns (out_device_bf16, dequantised q, k, v as fp64 numpy, desc)."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    from oracle import fp8 as ofp8
+    dev = device()
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    scale = 1.0 / math.sqrt(w.head_dim) if scale is None else scale
+    desc = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, "fp8")
+    cu = torch.from_numpy(desc.cu_seqlens).to(dev)
+    qd, kd, vd = (x.view(torch.uint8).to(dev) for x in (q8, k8, v8))
+    qsd, ksd, vsd = (torch.from_numpy(x).to(dev) for x in (qs, ks, vs))
+    out = torch.empty((w.total_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    pva.packed_attn_fwd_fp8(qd, kd, vd, qsd, ksd, vsd, cu, desc, scale, out, stream=stream)
+    torch.cuda.synchronize()
+    deq = [ofp8.dequantize(x.view(torch.uint8).numpy(), s, w.seq_len) for x, s in ((q8, qs), (k8, ks), (v8, vs))]
+    return out, deq[0], deq[1], deq[2], desc

@@ -1,0 +1,85 @@
+"""Parity of the HIP fp8 path (E4M3 Q/K/V with per-(sequence, head) fp32
+scales, fp8 MFMA, bf16 out) with the fp64 oracle run on the dequantised
+inputs. Tolerance: max abs error <= 6e-2 over every compared element; the
+mean is reported."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import FP8_MAX_ABS, err_stats, f64, run_fp8, sample_rows, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(w, tag):
+    say(f"[fp8] {tag}: T={w.text_len} I={w.image_len} H={w.num_heads}")
+    out, q, k, v, _ = run_fp8(w)
+    ref = oracle.packed_attention(q, k, v, w.text_len, w.image_len, 1.0 / math.sqrt(w.head_dim))
+    got = f64(out)
+    mx, mean = err_stats(got, ref)
+    say(f"[fp8] {tag}: max {mx:.3e} mean {mean:.3e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= FP8_MAX_ABS, (mx, mean)
+    return got, ref
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_fp8_random_packs(seed):
+    rng = np.random.default_rng(3000 + seed)
+    t, i = workloads.random_lengths(rng, int(rng.integers(1, 4)), 300, 500)
+    _full(workloads.custom(t, i, int(rng.choice([1, 3])), 128, seed=4000 + seed, dtype="fp8"), f"random{seed}")
+
+
+FP8_EDGES = {
+    "image_only": ([0], [200]),
+    "text_only": ([200], [0]),
+    "single_token": ([1], [0]),
+    "shorter_than_tile": ([3], [5]),
+    "text_crosses_tile": ([65], [63]),
+    "ragged_tail": ([70], [131]),
+    "many_short": ([1, 0, 5, 9, 2, 0, 33, 64], [0, 7, 1, 30, 0, 65, 1, 64]),
+    "long_text": ([700], [60]),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FP8_EDGES))
+def test_fp8_edges(name):
+    t, i = FP8_EDGES[name]
+    _full(workloads.custom(t, i, 2, 128, seed=78, dtype="fp8"), f"edge {name}")
+
+
+def test_fp8_full_size_sampled():
+    """The fp8 mixed-resolution batch at full size; sampled rows on four heads."""
+    w = workloads.mixed_res_fp8()
+    say(f"[fp8] full-size mixed batch N={w.total_tokens}")
+    out, q, k, v, _ = run_fp8(w)
+    got = out.float().cpu().numpy()
+    rng = np.random.default_rng(9)
+    heads = sorted({0, w.num_heads - 1, int(rng.integers(0, w.num_heads)), int(rng.integers(0, w.num_heads))})
+    off = oracle.offsets(w.seq_len)
+    worst, total, count = 0.0, 0.0, 0
+    for s in range(w.nseq):
+        rows = sample_rows(w.text_len[s], w.seq_len[s], rng)
+        ref = oracle.packed_attention_rows(q, k, v, w.text_len, w.image_len, 1.0 / math.sqrt(w.head_dim),
+                                           s, rows, heads)
+        d = np.abs(got[off[s] + np.array(rows)][:, heads].astype(np.float64) - ref)
+        worst = max(worst, float(d.max()))
+        total += float(d.sum())
+        count += d.size
+    say(f"[fp8] full-size: max {worst:.3e} mean {total / count:.3e} over {count} elements")
+    assert np.all(np.isfinite(got))
+    assert worst <= FP8_MAX_ABS
+
+
+def test_fp8_first_text_row_is_v0():
+    """Text row 0 sees key 0 only: its output is v0 (dequantised) up to the bf16 output rounding."""
+    w = workloads.custom([40, 40], [100, 100], 2, 128, seed=79, dtype="fp8")
+    out, q, k, v, _ = run_fp8(w)
+    got = f64(out)
+    off = oracle.offsets(w.seq_len)
+    for s in range(w.nseq):
+        ref = v[off[s]]
+        assert np.max(np.abs(got[off[s]] - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2 ** -8
