@@ -32,6 +32,15 @@ import workloads  # noqa: E402
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}  # MI355X dense MFMA, 256 CU x 2.4 GHz
 PEAK_HBM_GBS = 8000.0
 
+CSRC = os.path.join(ROOT, "packed_varlen_masked_attn_amd", "csrc")
+# Sources that decide each kernel's code: a stored counter reading is only
+# reported while their hash is unchanged.
+KERNEL_SOURCES = {
+    "bf16": ["fwd_bf16.hip", "kernel_common.h", "pva_internal.h", "plan.cpp"],
+    "fp8": ["fwd_fp8.hip", "kernel_common.h", "pva_internal.h", "plan.cpp"],
+}
+PROFILES = os.path.join(ROOT, "profiles")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -55,7 +64,96 @@ def parse():
     ap.add_argument("--kernel-only", action="store_true", help="time the kernel only (for profilers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of --kernel-only runs "
+                         "(no GPU needed) and print the traffic record for --workload")
     return ap.parse_args()
+
+
+def kernel_source_hash(dtype):
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[dtype]:
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(dtype, workload):
+    return os.path.join(PROFILES, f"hbm_traffic_fwd_{dtype}_{workload}.txt")
+
+
+def _counter_rows(path, counter):
+    import csv
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row["Counter_Name"] == counter:
+                yield row["Kernel_Name"], float(row["Counter_Value"])
+
+
+def pmc_summary(args):
+    """HBM bytes per launch of the attention kernel from rocprofv3 counter
+    files: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each divided by what
+    the same counter reads per byte for a plain 1 GiB device copy."""
+    fetch_csv, write_csv, cfetch_csv, cwrite_csv = args.pmc_summary
+    w = workloads.WORKLOADS[args.workload]()
+    dtype = "fp8" if w.dtype == "fp8" else "bf16"
+    tag = f"fwd_{dtype}_kernel"
+    copy_bytes = float(1 << 30)
+    cf = [v for k, v in _counter_rows(cfetch_csv, "FETCH_SIZE") if "copyBuffer" in k]
+    cw = [v for k, v in _counter_rows(cwrite_csv, "WRITE_SIZE") if "copyBuffer" in k]
+    kf = [v for k, v in _counter_rows(fetch_csv, "FETCH_SIZE") if tag in k]
+    kw = [v for k, v in _counter_rows(write_csv, "WRITE_SIZE") if tag in k]
+    if not (cf and cw and kf and kw):
+        sys.exit("pmc summary: a counter file holds no matching dispatch")
+    f_fac = statistics.fmean(cf) * 1024.0 / copy_bytes  # counter bytes per byte read
+    w_fac = statistics.fmean(cw) * 1024.0 / copy_bytes
+    fetch = statistics.fmean(kf) * 1024.0 / f_fac
+    write = statistics.fmean(kw) * 1024.0 / w_fac
+    lines = [
+        f"kernel: {tag}",
+        f"workload: {w.name}",
+        f"source_sha256_16: {kernel_source_hash(dtype)}",
+        f"dispatches: fetch {len(kf)}, write {len(kw)}",
+        f"raw_fetch_kib_per_dispatch: {statistics.fmean(kf):.1f}",
+        f"raw_write_kib_per_dispatch: {statistics.fmean(kw):.1f}",
+        f"copy_fetch_factor: {f_fac:.4f}",
+        f"copy_write_factor: {w_fac:.4f}",
+        f"fetch_bytes_per_launch: {fetch:.0f}",
+        f"write_bytes_per_launch: {write:.0f}",
+        f"traffic_bytes_per_launch: {fetch + write:.0f}",
+        f"algorithmic_bytes_per_launch: {algorithmic_bytes(w)}",
+    ]
+    print("\n".join(lines))
+
+
+def algorithmic_bytes(w):
+    """Q, K, V read once and O written once (fp8: 1-byte inputs, bf16 output),
+    plus the per-(sequence, head) scales of the fp8 path."""
+    n_el = w.total_tokens * w.num_heads * w.head_dim
+    if w.dtype == "fp8":
+        return 3 * n_el + 2 * n_el + 3 * 4 * w.nseq * w.num_heads
+    return 4 * 2 * n_el
+
+
+def stored_traffic(dtype, workload):
+    """Traffic record for this kernel and workload if its counters were taken
+    on the current sources, else None."""
+    path = traffic_file(dtype, workload)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line:
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("source_sha256_16") != kernel_source_hash(dtype):
+        return None
+    try:
+        return int(rec["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def copy_calibration():
@@ -78,6 +176,10 @@ def main():
               "(a multi-GPU run would shard heads or sequences, which is not built). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.pmc_summary:
+        pmc_summary(args)
+        return
 
     import torch
     import packed_varlen_masked_attn_amd as pva
@@ -181,8 +283,9 @@ def main():
         "peak": PEAK_TFLOPS[dtype],
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
-        "traffic": None,
+        "traffic": stored_traffic(dtype, w.name),
         "kernel": "fwd_fp8_kernel<128>" if is_fp8 else f"fwd_bf16_kernel<{D}>",
+        "algorithmic_bytes": algorithmic_bytes(w),
     }
     if args.kernel_only:
         print(json.dumps(result), flush=True)

@@ -1,0 +1,72 @@
+"""Host-side pieces of bench.py: the single-GPU guard and the HBM counter summary."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+HEADER = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+          "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+          "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+
+
+def _csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(HEADER)
+        for i, (kernel, counter, value) in enumerate(rows):
+            w.writerow([i, i, "Agent 1", 1, 1, 1, 256, 1, kernel, 256, 0, 0, 8, 0, 16, counter, value, 0, 1])
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+def test_pmc_summary_scales_by_copy_calibration(tmp_path, capsys):
+    gib_kib = (1 << 30) / 1024
+    k = "_ZN3pva12_GLOBAL__N_115fwd_bf16_kernelILi128EEEv"
+    _csv(tmp_path / "f.csv", [("other", "FETCH_SIZE", 5.0), (k, "FETCH_SIZE", 1000.0), (k, "FETCH_SIZE", 3000.0)])
+    _csv(tmp_path / "w.csv", [(k, "WRITE_SIZE", 4000.0)])
+    _csv(tmp_path / "cf.csv", [("__amd_rocclr_copyBuffer", "FETCH_SIZE", gib_kib / 2)])
+    _csv(tmp_path / "cw.csv", [("__amd_rocclr_copyBuffer", "WRITE_SIZE", gib_kib)])
+
+    class A:
+        workload = "tiny"
+        pmc_summary = [str(tmp_path / n) for n in ("f.csv", "w.csv", "cf.csv", "cw.csv")]
+    bench.pmc_summary(A)
+    rec = dict(line.split(": ", 1) for line in capsys.readouterr().out.strip().splitlines())
+    assert float(rec["copy_fetch_factor"]) == pytest.approx(0.5)
+    # mean 2000 KiB fetched per dispatch at factor 0.5 -> 4000 KiB; 4000 KiB written at factor 1
+    assert int(rec["fetch_bytes_per_launch"]) == 4000 * 1024
+    assert int(rec["write_bytes_per_launch"]) == 4000 * 1024
+    assert int(rec["traffic_bytes_per_launch"]) == 8000 * 1024
+
+
+def test_stored_traffic_requires_current_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    path = bench.traffic_file("bf16", "wl")
+    with open(path, "w") as f:
+        f.write(f"# comment: ignored\nsource_sha256_16: {bench.kernel_source_hash('bf16')}\n"
+                "traffic_bytes_per_launch: 12345\n")
+    assert bench.stored_traffic("bf16", "wl") == 12345
+    with open(path, "w") as f:
+        f.write("source_sha256_16: 0000000000000000\ntraffic_bytes_per_launch: 12345\n")
+    assert bench.stored_traffic("bf16", "wl") is None
+    assert bench.stored_traffic("fp8", "missing") is None
+
+
+def test_algorithmic_bytes():
+    import workloads
+    w = workloads.WORKLOADS["mixed_res"]()
+    assert bench.algorithmic_bytes(w) == 4 * 2 * 25072 * 32 * 128
+    w8 = workloads.WORKLOADS["mixed_res_fp8"]()
+    assert bench.algorithmic_bytes(w8) == 5 * 25072 * 32 * 128 + 12 * 8 * 32
