@@ -52,41 +52,36 @@ struct Bf16Cfg {
   static constexpr int C = D / 8;          // 16-byte chunks per K/V row
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
-  static constexpr int TILE = BN * D * 2;  // bytes of one K or V tile
-  // 16-byte DMA rounds per wave per tile and tensor; when a tile has fewer
-  // chunks than the workgroup has lanes, only the first waves issue one
-  static constexpr int NLD = (BN * C + NT - 1) / NT;
-  static_assert((BN * C) % 64 == 0 && (BN * C >= NT ? (BN * C) % NT == 0 : true), "whole wave-sized DMA");
   static constexpr int NS = 4;             // LDS stages per tensor
   // K rows are padded by one 16-byte chunk: the 16 consecutive rows a K
   // operand read touches at one chunk then fall on 16 different bank groups,
   // and the address stays affine in the chunk (one base register).
   static constexpr int KROW = C + 1;                        // chunks per padded K row
-  static constexpr int KSLOTS = BN * KROW;                  // 16-byte slots of a K tile
+  // 16-byte slots of a K / V stage, rounded up to whole 64-lane DMA rounds
+  static constexpr int KSLOTS = (BN * KROW + 63) / 64 * 64;
   static constexpr int KTILE = KSLOTS * 16;
-  static constexpr int NLDK = (KSLOTS + NT - 1) / NT;       // K DMA rounds (the last may be partial)
   // V rows are padded by 64 bytes: the four consecutive rows a transpose read
   // touches then sit in four different 64-byte quarters of the bank window,
   // and the address stays affine in the column block (one base register).
   static constexpr int VROW = C + 4;                        // chunks per padded V row
-  static constexpr int VSLOTS = BN * VROW;                  // 16-byte slots of a V tile
+  static constexpr int VSLOTS = (BN * VROW + 63) / 64 * 64;
   static constexpr int VTILE = VSLOTS * 16;
-  static constexpr int NLDV = (VSLOTS + NT - 1) / NT;       // V DMA rounds (the last may be partial)
   // DMA instructions every wave issues per tile (some waves issue one more);
   // the partial vmcnt waits count only these, so waves with more loads in
   // flight simply wait a little longer
   static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
+  static_assert(QB == 2 || 2 * (KTILE + VTILE) * NS <= 160 * 1024, "two workgroups per CU");
 };
 
 template <int D>
 struct Kernel {
   using Cfg = Bf16Cfg<D>;
-  static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD;
+  static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
 
   // ---- K and V tiles: rows padded to KROW / VROW 16-byte slots
-  using KLoader = DmaLoader<Cfg::NT, BN, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
-  using VLoader = DmaLoader<Cfg::NT, BN, Cfg::VROW, Cfg::VSLOTS, PaddedRows<C>>;
+  using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
+  using VLoader = BufLoader<Cfg::NT, Cfg::VROW, Cfg::VSLOTS, PaddedRows<C>>;
 
   // ---- K operands of one tile: row l32, chunk 2c + g
   static __device__ __forceinline__ void read_k(bf16x8 (&a)[NKC], const uint8_t* kst, int l32, int g) {
@@ -307,7 +302,7 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   using Kn = Kernel<D>;
   using Cfg = typename Kn::Cfg;
   using s16x8 = typename Kn::s16x8;
-  constexpr int BN = Cfg::BN, QB = Cfg::QB, NKC = Cfg::NKC, NDB = Cfg::NDB, NLD = Cfg::NLD, NS = Cfg::NS;
+  constexpr int BN = Cfg::BN, QB = Cfg::QB, NKC = Cfg::NKC, NDB = Cfg::NDB, NS = Cfg::NS;
   static_assert(NS == 4, "the loop below is unrolled for a ring of four stages");
   // separate arrays per stage: the compiler sees that an LDS DMA into one
   // stage and reads of another do not alias
@@ -326,7 +321,9 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   const int g = lane >> 5, l32 = lane & 31;
   const int T = it.text_len, L = it.seq_len;
   const int64_t rs = int64_t(H) * D;  // elements between consecutive tokens of one head
-  const int64_t rs2 = rs * 2;         // bytes
+  const uint32_t rs2 = uint32_t(rs) * 2u;  // bytes (the planner keeps L * rs2 below 2^31)
+  // bytes from a head's first row of the sequence to the end of its last row
+  const uint32_t head_bytes = uint32_t(L - 1) * rs2 + 2u * D;
   const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
   const __bf16* Qh = Q + base;
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
@@ -345,12 +342,21 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   const int kend = it.k_end;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
+  // (tile t's resource starts at key row t * BN and ends with the sequence)
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;
-  kld.init(rs2, wave, lane);
-  vld.init(rs2, wave, lane);
-  auto ld_k = [&](int t, uint8_t* stage) { kld.load(Kb, t * BN, L, rs2, stage, wave, lane); };
-  auto ld_v = [&](int t, uint8_t* stage) { vld.load(Vb, t * BN, L, rs2, stage, wave, lane); };
+  // V's extra DMA rounds go to the waves that issue none for K
+  const int vwave = (wave + Cfg::NW / 2) % Cfg::NW;
+  kld.init(rs2, lane, wave);
+  vld.init(rs2, lane, vwave);
+  auto ld_k = [&](int t, uint8_t* stage) {
+    const uint32_t o = uint32_t(t * BN) * rs2;
+    kld.load(make_rsrc(Kb + o, head_bytes - o), stage, wave);
+  };
+  auto ld_v = [&](int t, uint8_t* stage) {
+    const uint32_t o = uint32_t(t * BN) * rs2;
+    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, vwave);
+  };
   if (kend > 0) ld_k(0, kst[0]);
   if (kend > 1) ld_k(1, kst[1]);
   if (kend > 0) ld_v(0, vst[0]);

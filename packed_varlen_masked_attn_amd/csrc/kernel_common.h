@@ -123,6 +123,50 @@ struct DmaLoader {
   static constexpr int MIN_PER_WAVE = SLOTS / NT;
 };
 
+// Buffer resource over the bytes [base, base + bytes) (raw, no stride):
+// loads at offsets at or past `bytes` return zeros instead of touching
+// memory. gfx9 resource word 3 (data format 32, no swizzle).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+// An offset that is out of range of every resource built by make_rsrc for
+// fewer than 2^31 bytes: its loads write zeros.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+// Global -> LDS DMA of one key tile through a buffer resource whose range
+// ends at the last byte of the sequence's rows of this head: rows past the
+// sequence end read as zeros, so the tile needs neither clamping nor a slow
+// path. The tile occupies SLOTS 16-byte slots (ROW per key row, SLOTS a
+// multiple of 64); lane `lane` of wave-round (i, wave) fills slot
+// NT * i + 64 * wave + lane. Slot s holds chunk Map::chunk(r, s % ROW) of tile
+// row r = s / ROW; pad slots (chunk -1) get an out-of-range offset and are
+// written with zeros. A wave whose round starts past the tile skips it (a
+// scalar branch). Per lane, only a constant 32-bit offset per round is kept.
+template <int NT, int ROW, int SLOTS, typename Map>
+struct BufLoader {
+  static_assert(SLOTS % 64 == 0, "whole-wave rounds");
+  static constexpr int ROUNDS = (SLOTS + NT - 1) / NT;
+  uint32_t off[ROUNDS];
+  __device__ __forceinline__ void init(uint32_t rs2, int lane, int wave) {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int s = NT * i + 64 * wave + lane;
+      const int r = s / ROW, c = Map::chunk(r, s % ROW);
+      off[i] = (s < SLOTS && c >= 0) ? uint32_t(r) * rs2 + 16u * uint32_t(c) : kOutOfRange;
+    }
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, uint8_t* stage, int wave) const {
+#pragma unroll
+    for (int i = 0; i < ROUNDS; ++i) {
+      const int s0 = NT * i + 64 * wave;
+      if (NT * (i + 1) > SLOTS && s0 >= SLOTS) continue;  // only the last round can be partial
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (PVA_LDS void*)(stage + 16 * s0), 16, off[i], 0, 0, 0);
+    }
+  }
+  // DMA instructions every wave issues per tile (some waves issue one more)
+  static constexpr int MIN_PER_WAVE = SLOTS / NT;
+};
+
 // Row-padded layout: the first CHUNKS slots of a row are the row's chunks in
 // order, the rest are pad.
 template <int CHUNKS>

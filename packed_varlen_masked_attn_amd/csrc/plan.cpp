@@ -69,6 +69,10 @@ int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, 
     if (T < 0 || I < 0) return fail(err, PVA_ERR_INVALID_ARG, "text_len and image_len must be >= 0");
     if (T + I < 1) return fail(err, PVA_ERR_INVALID_ARG, "every sequence needs at least one token");
     if (T + I > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
+    // the kernels address one head's rows of a sequence with 32-bit byte
+    // offsets below 2^31 (row stride H * D elements of at most 2 bytes)
+    if ((T + I) * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
+      return fail(err, PVA_ERR_UNSUPPORTED, "sequence too long for 32-bit head addressing (L * H * D * 2 >= 2^31)");
     total += T + I;
     if (total > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "packed token count exceeds int32");
     p.seq_len[s] = static_cast<int32_t>(T + I);

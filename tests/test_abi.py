@@ -64,7 +64,9 @@ def _build_host(t, i, H=2, D=128, dtype=0):
     ([4], [4], 2, 96, 0, pva.PVA_ERR_UNSUPPORTED),            # D not in {64, 128}
     ([4], [4], 2, 64, 1, pva.PVA_ERR_UNSUPPORTED),            # fp8 with D = 64
     ([4], [4], 2, 128, 7, pva.PVA_ERR_INVALID_ARG),           # unknown dtype
-    ([2 ** 30, 2 ** 30], [0, 1], 1, 64, 0, pva.PVA_ERR_INVALID_ARG),  # N overflows int32
+    ([2 ** 24 - 1] * 129, [0] * 129, 1, 64, 0, pva.PVA_ERR_INVALID_ARG),  # N overflows int32
+    ([2 ** 24], [0], 1, 64, 0, pva.PVA_ERR_UNSUPPORTED),      # L * H * D * 2 = 2^31
+    ([100], [2 ** 20], 16, 64, 0, pva.PVA_ERR_UNSUPPORTED),   # L * H * D * 2 > 2^31
 ])
 def test_build_rejects(t, i, H, D, dtype, code):
     if t:
