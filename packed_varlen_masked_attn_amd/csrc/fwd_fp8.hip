@@ -76,8 +76,8 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 struct Fp8Kernel {
   using Cfg = Fp8Cfg;
   static constexpr int BN = Cfg::BN, NB = Cfg::NB, C = Cfg::C, NKS = Cfg::NKS, NDB = Cfg::NDB;
-  using KLoader = DmaLoader<Cfg::NT, BN, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
-  using VLoader = DmaLoader<Cfg::NT, BN, Cfg::VROW, Cfg::VSLOTS, VSwizzledPairs>;
+  using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
+  using VLoader = BufLoader<Cfg::NT, Cfg::VROW, Cfg::VSLOTS, VSwizzledPairs>;
 
   // K operand of 64-wide step c for key block b: row 32 b + l32, bytes
   // 64 c + 32 g .. +31 (any d assignment works as long as Q uses the same)
@@ -240,6 +240,9 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const int g = lane >> 5, l32 = lane & 31;
   const int T = it.text_len, L = it.seq_len;
   const int64_t rs = int64_t(H) * D;  // bytes (one byte per element) between tokens of one head
+  const uint32_t rs32 = uint32_t(rs);  // the planner keeps L * rs below 2^31
+  // bytes from a head's first row of the sequence to the end of its last row
+  const uint32_t head_bytes = uint32_t(L - 1) * rs32 + uint32_t(D);
   const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
   const uint8_t* Qh = Q + base;
   const uint8_t* Kb = K + base;
@@ -257,10 +260,18 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
 
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;
-  kld.init(rs, wave, lane);
-  vld.init(rs, wave, lane);
-  auto ld_k = [&](int t, uint8_t* stage) { kld.load(Kb, t * BN, L, rs, stage, wave, lane); };
-  auto ld_v = [&](int t, uint8_t* stage) { vld.load(Vb, t * BN, L, rs, stage, wave, lane); };
+  // tile t's buffer resource starts at key row t * BN and ends with the
+  // sequence: rows past the end read as zeros
+  kld.init(rs32, lane, wave);
+  vld.init(rs32, lane, wave);
+  auto ld_k = [&](int t, uint8_t* stage) {
+    const uint32_t o = uint32_t(t * BN) * rs32;
+    kld.load(make_rsrc(Kb + o, head_bytes - o), stage, wave);
+  };
+  auto ld_v = [&](int t, uint8_t* stage) {
+    const uint32_t o = uint32_t(t * BN) * rs32;
+    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, wave);
+  };
   if (kend > 0) ld_k(0, kst[0]);
   if (kend > 1) ld_k(1, kst[1]);
   if (kend > 0) ld_v(0, vst[0]);

@@ -24,22 +24,6 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 // and l always share the same reference max.
 constexpr float kLazyRescale = 8.0f;
 
-// LDS layout of a streamed K or V tile: row r (a key), 16-byte chunk c of the
-// head dimension. Chunks are XOR-permuted per row so that the MFMA operand
-// reads hit distinct banks:
-//  * K is read 16 bytes per lane, 16 consecutive rows per LDS cycle: the
-//    swizzle maps the same chunk of those 16 rows onto 16 different chunks;
-//  * V is read with ds_read_b64_tr_b16, 4 rows x 64 bytes per half-wave: the
-//    swizzle moves each of 4 consecutive rows to a different 64-byte quarter.
-template <int C>  // C = 16-byte chunks per row (D / 8)
-__device__ __forceinline__ int swz_k(int r) {
-  return ((r * C) / 16) % C;
-}
-template <int C>
-__device__ __forceinline__ int swz_v(int r) {
-  return 4 * (((r * C) / 16) % (C / 4));
-}
-
 // Maximum over the two 32-lane halves of a wave: permlane32_swap(x, x) hands
 // each lane its own value and its partner's (lane ^ 32) in some order.
 __device__ __forceinline__ float half_swap_max(float x) {
@@ -73,54 +57,6 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 struct RowState {
   float m;  // reference max (log2 units); O and l are relative to it
   float l;  // this lane's partial row sum (the other half-wave holds the rest)
-};
-
-// Direct global -> LDS DMA of one key tile (BN rows of a K or V head slice)
-// into a tile of ROW 16-byte slots per row (SLOTS slots in all). Lane writes
-// 16 B at stage + 16 * slot; slot s holds tile row s / ROW at slot position
-// s % ROW, which Map::chunk(row, pos) maps to the global 16-byte chunk it
-// carries, or to -1 for a pad slot. Lanes on pad slots or past the tile are
-// switched off, so nothing is fetched or written for them. In steady state
-// the tile base is a scalar and each lane adds a constant 32-bit offset; the
-// last tile of a sequence clamps rows to the sequence end (finite data that
-// the mask discards).
-template <int NT, int BN, int ROW, int SLOTS, typename Map>
-struct DmaLoader {
-  static constexpr int ROUNDS = (SLOTS + NT - 1) / NT;
-  uint32_t off[ROUNDS];  // per-round lane offset within the tile (bytes)
-  bool act[ROUNDS];      // lane carries data
-  __device__ __forceinline__ void init(int64_t rs2, int wave, int lane) {
-#pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) {
-      const int s = NT * i + 64 * wave + lane;
-      const int r = s / ROW, c = Map::chunk(r, s % ROW);
-      act[i] = s < SLOTS && c >= 0;
-      off[i] = act[i] ? uint32_t(r * rs2 + 16 * c) : 0u;
-    }
-  }
-  // one round (a no-op for waves whose round starts past the tile)
-  __device__ __forceinline__ void round(int i, const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
-                                        int wave, int lane) const {
-    const int s0 = NT * i + 64 * wave;
-    if (s0 >= SLOTS) return;
-    if (!act[i]) return;
-    const uint8_t* src;
-    if (k0 + BN <= L) {
-      src = seq_base + int64_t(k0) * rs2 + off[i];
-    } else {
-      const int s = s0 + lane, r = s / ROW;
-      src = seq_base + int64_t(min(k0 + r, L - 1)) * rs2 + 16 * Map::chunk(r, s % ROW);
-    }
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (PVA_LDS void*)(stage + 16 * s0), 16, 0, 0);
-  }
-  __device__ __forceinline__ void load(const uint8_t* seq_base, int k0, int L, int64_t rs2, uint8_t* stage,
-                                       int wave, int lane) const {
-#pragma unroll
-    for (int i = 0; i < ROUNDS; ++i) round(i, seq_base, k0, L, rs2, stage, wave, lane);
-  }
-  // DMA instructions every wave issues per tile (some waves issue one more)
-  static constexpr int MIN_PER_WAVE = SLOTS / NT;
 };
 
 // Buffer resource over the bytes [base, base + bytes) (raw, no stride):
@@ -163,8 +99,6 @@ struct BufLoader {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (PVA_LDS void*)(stage + 16 * s0), 16, off[i], 0, 0, 0);
     }
   }
-  // DMA instructions every wave issues per tile (some waves issue one more)
-  static constexpr int MIN_PER_WAVE = SLOTS / NT;
 };
 
 // Row-padded layout: the first CHUNKS slots of a row are the row's chunks in
