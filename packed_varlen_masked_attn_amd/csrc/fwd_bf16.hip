@@ -6,16 +6,16 @@
 // challenge) and Model structure item 1 (Generalized Causal Attention: causal
 // text prefix, bidirectional image block that sees the whole prefix).
 //
-// One workgroup = 4 waves = one work item (sequence, head, 256 query rows);
-// one wave per SIMD, each owning 64 query rows as two 32-row blocks that share
-// every K and V operand read. Keys are streamed in tiles of 32.
+// One workgroup = 4 waves = one work item (sequence, head, 128 query rows);
+// each wave owns 32 query rows, two workgroups share a CU (two waves per
+// SIMD). Keys are streamed in tiles of 32.
 //
 // Per wave and key tile j, on 32x32x16 bf16 MFMA:
 //   S^T[key, q] = K Q^T    A = K from LDS (16-byte reads), B = Q^T held in
 //                          registers for the whole item. Each lane then owns
-//                          one query column of each block, so row max and
-//                          row sum are in-lane plus one exchange between the
-//                          two 32-lane halves.
+//                          one query column, so row max and row sum are
+//                          in-lane plus one exchange between the two 32-lane
+//                          halves.
 //   online softmax in fp32, log2 domain, lazy rescaling of O and l.
 //   O^T[d, q] += V^T P^T   B = P^T straight from the S^T accumulators (cast to
 //                          bf16, no shuffle: the contraction order of the keys
@@ -23,10 +23,12 @@
 //                          row-major V tile with ds_read_b64_tr_b16.
 //
 // Software pipeline (iteration j, one barrier each):
-//   issue global->LDS loads of K(j+NS) and V(j+NS-1) (direct LDS DMA)
-//   [S(j+1) MFMAs]  interleaved with  [exp / row sums / bf16 cast of tile j]
+//   issue global->LDS loads of K(j+NS) and V(j+NS-1) (buffer loads straight
+//   into LDS; rows past the sequence end read as zeros)
+//   phase 1: [S(j+1) MFMAs] next to [exp / bf16 packing of tile j]; the V^T
+//            operands of PV(j) are read from LDS here as well
 //   (partial tiles only) element mask of tile j+1
-//   [PV(j) MFMAs]   interleaved with  [row max of tile j+1]
+//   phase 2: [PV(j) MFMAs] next to [row sums of tile j, row max of tile j+1]
 //   rare branch: rescale O and l when a row's reference max moved
 //   wait for the loads of K(j+2) and V(j+1) only; later ones stay in flight
 // K and V each have a ring of NS LDS stages, so every load has NS-1
@@ -36,19 +38,14 @@
 
 #include "kernel_common.h"
 
-#ifndef PVA_BF16_QB
-#define PVA_BF16_QB 1  // 32-row query blocks per wave: 1 (2 waves/SIMD) or 2 (1 wave/SIMD)
-#endif
-
 namespace pva {
 
 namespace {
 
 template <int D>
 struct Bf16Cfg {
-  static constexpr int QB = PVA_BF16_QB;   // 32-row query blocks per wave
-  static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = BM / (32 * QB), NT = 64 * NW;
-  static_assert(BM == NW * QB * 32 && BN == 32, "waves x 32-row query blocks; 32-key tiles");
+  static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = BM / 32, NT = 64 * NW;
+  static_assert(BM % 32 == 0 && BN == 32, "one 32-row query block per wave; 32-key tiles");
   static constexpr int C = D / 8;          // 16-byte chunks per K/V row
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
@@ -70,144 +67,33 @@ struct Bf16Cfg {
   // the partial vmcnt waits count only these, so waves with more loads in
   // flight simply wait a little longer
   static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
-  static_assert(QB == 2 || 2 * (KTILE + VTILE) * NS <= 160 * 1024, "two workgroups per CU");
+  static_assert(2 * (KTILE + VTILE) * NS <= 160 * 1024, "two workgroups per CU");
 };
+
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
 
 template <int D>
 struct Kernel {
   using Cfg = Bf16Cfg<D>;
-  static constexpr int BN = Cfg::BN, QB = Cfg::QB, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB;
+  static constexpr int BN = Cfg::BN, C = Cfg::C, NKC = Cfg::NKC, NDB = Cfg::NDB;
   typedef short s16x8 __attribute__((ext_vector_type(8)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
   // ---- K and V tiles: rows padded to KROW / VROW 16-byte slots
   using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
   using VLoader = BufLoader<Cfg::NT, Cfg::VROW, Cfg::VSLOTS, PaddedRows<C>>;
 
-  // ---- K operands of one tile: row l32, chunk 2c + g
-  static __device__ __forceinline__ void read_k(bf16x8 (&a)[NKC], const uint8_t* kst, int l32, int g) {
-#pragma unroll
-    for (int c = 0; c < NKC; ++c)
-      a[c] = *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * Cfg::KROW + 2 * c + g));
+  // ---- K operand of d-chunk c: row l32, chunk 2c + g of the padded tile
+  static __device__ __forceinline__ bf16x8 read_k(const uint8_t* kst, int c, int l32, int g) {
+    return *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * Cfg::KROW + 2 * c + g));
   }
 
-  // ---- V^T operands of one tile: for 16-key step kc and 32-column block db
-  static __device__ __forceinline__ void read_v(s16x8 (&a)[2][NDB], const uint8_t* vst, int v_row0, int v_col) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) a[kc][db] = read_v_step(vst, kc * NDB + db, v_row0, v_col);
-  }
-
-  // ---- S^T = K Q^T for both query blocks (two independent MFMA chains)
-  static __device__ __forceinline__ void s_mfma(f32x16 (&s)[QB], const bf16x8 (&a)[NKC],
-                                                const bf16x8 (&qf)[QB][NKC]) {
-#pragma unroll
-    for (int h = 0; h < QB; ++h) s[h] = f32x16{};
-#pragma unroll
-    for (int c = 0; c < NKC; ++c)
-#pragma unroll
-      for (int h = 0; h < QB; ++h) s[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c], qf[h][c], s[h], 0, 0, 0);
-  }
-
-  // ---- O^T += V^T P^T for both query blocks
-  static __device__ __forceinline__ void pv_mfma(f32x16 (&o)[QB][NDB], const s16x8 (&a)[2][NDB],
-                                                 const bf16x8 (&pb)[QB][2]) {
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int h = 0; h < QB; ++h)
-          o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[kc][db]), pb[h][kc],
-                                                             o[h][db], 0, 0, 0);
-  }
-
-  // ---- instruction interleaving hints for the scheduler (same basic block)
-  // masks: 0x008 MFMA, 0x002 VALU, 0x080 any LDS, 0x100 LDS read
-  static __device__ __forceinline__ void schedule_s_with_exp() {
-    __builtin_amdgcn_sched_group_barrier(0x100, NKC, 0);
-#pragma unroll
-    for (int i = 0; i < QB * NKC; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 7, 0);
-    }
-  }
-  static __device__ __forceinline__ void schedule_pv_with_max() {
-    __builtin_amdgcn_sched_group_barrier(0x080, 4 * NDB, 0);
-#pragma unroll
-    for (int i = 0; i < 2 * QB * NDB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-    }
-  }
-
-  // ---- an empty asm that consumes the probabilities: the compiler must have
-  // them in registers at this point, so it cannot sink their computation past
-  // the following branch into the PV block
-  static __device__ __forceinline__ void pin(bf16x8 (&pb)[QB][2], float (&psum)[QB]) {
-#pragma unroll
-    for (int h = 0; h < QB; ++h) {
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        i32x4 v = __builtin_bit_cast(i32x4, pb[h][k]);
-        asm volatile("" : "+v"(v));
-        pb[h][k] = __builtin_bit_cast(bf16x8, v);
-      }
-      asm volatile("" : "+v"(psum[h]));
-    }
-  }
-
-  // ---- S(j+1) = K Q^T for both query blocks, interleaved in program order
-  // with the probabilities of tile j: per d-chunk c, one K read two chunks
-  // ahead, two MFMAs (one per query block), then four exponentials.
-  static __device__ __forceinline__ void s_with_probs(f32x16 (&snext)[QB], const uint8_t* kst,
-                                                      const bf16x8 (&qf)[QB][NKC], const f32x16 (&scur)[QB],
-                                                      float scale_log2, const RowState (&st)[QB],
-                                                      bf16x8 (&pb)[QB][2], float (&psum)[QB], int l32, int g) {
-    constexpr int PER_C = (QB * 16 + NKC - 1) / NKC;  // exponentials per d-chunk
-    const uint8_t* krow = kst + 16 * (l32 * Cfg::KROW + g);
-    auto rd = [&](int c) { return *reinterpret_cast<const bf16x8*>(krow + 32 * c); };
-    bf16x8 ka[3];
-    ka[0] = rd(0);
-    if (NKC > 1) ka[1] = rd(1);
-#pragma unroll
-    for (int h = 0; h < QB; ++h) snext[h] = f32x16{};
-    float part[QB][2];
-#pragma unroll
-    for (int h = 0; h < QB; ++h) part[h][0] = part[h][1] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      if (c + 2 < NKC) ka[(c + 2) % 3] = rd(c + 2);
-#pragma unroll
-      for (int h = 0; h < QB; ++h)
-        snext[h] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % 3], qf[h][c], snext[h], 0, 0, 0);
-#pragma unroll
-      for (int e = 0; e < PER_C; ++e) {
-        const int idx = c * PER_C + e;  // element of the (QB x 16) probability tile
-        if (idx < QB * 16) {
-          const int h = idx / 16, i = idx % 16;
-          pb[h][i / 8][i % 8] = (__bf16)fast_exp2(fmaf(scur[h][i], scale_log2, -st[h].m));
-          if (i % 2 == 1) {
-            // row sum of the bf16 probabilities PV actually uses, two at a time
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            const bf16x2 pair = {pb[h][i / 8][i % 8 - 1], pb[h][i / 8][i % 8]};
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-            part[h][(i / 2) % 2] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[h][(i / 2) % 2], false);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < QB; ++h) psum[h] = part[h][0] + part[h][1];
-    pin(pb, psum);
-  }
-
-  // ---- O^T += V^T P^T for both query blocks, interleaved in program order
-  // with the row max of tile j+1: per (kc, db) step, one V^T operand read two
-  // steps ahead, two MFMAs, then a few max operations.
+  // ---- V^T operand of PV step `step` (16-key step kc, 32-column block db):
+  // rows 16 kc + v_row0 (+8), columns 32 db + v_col .. +3 of the padded tile
   static __device__ __forceinline__ s16x8 read_v_step(const uint8_t* vst, int step, int v_row0, int v_col) {
     const int kc = step / NDB, db = step % NDB;
-    // rows 16 kc + v_row0 (+8), columns 32 db + v_col .. +3 of the padded tile
     const uint8_t* p0 = vst + 16 * Cfg::VROW * (16 * kc + v_row0) + 2 * (32 * db + v_col);
     const uint8_t* p1 = p0 + 16 * Cfg::VROW * 8;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
@@ -215,94 +101,141 @@ struct Kernel {
     return s16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
-  // `va0`, `va1`: the operands of steps 0 and 1, read early by the caller.
-  static __device__ __forceinline__ void pv_with_max(f32x16 (&o)[QB][NDB], const uint8_t* vst,
-                                                     const bf16x8 (&pb)[QB][2], const f32x16 (&snext)[QB],
-                                                     float scale_log2, float (&mt)[QB], int v_row0, int v_col,
-                                                     s16x8 va0, s16x8 va1) {
-    constexpr int NSTEP = 2 * NDB;
-    auto rd = [&](int step) { return read_v_step(vst, step, v_row0, v_col); };
-    s16x8 va[3];
-    va[0] = va0;
-    va[1] = va1;
-    float mx[QB];
+  // ---- S^T = K Q^T of one tile (prologue only; the loop interleaves it)
+  static __device__ __forceinline__ f32x16 s_tile(const uint8_t* kst, const bf16x8 (&qf)[NKC], int l32, int g) {
+    f32x16 s = {};
 #pragma unroll
-    for (int h = 0; h < QB; ++h) mx[h] = snext[h][0];
-    constexpr int PER_STEP = (QB * 15 + NSTEP - 1) / NSTEP;
+    for (int c = 0; c < NKC; ++c)
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(kst, c, l32, g), qf[c], s, 0, 0, 0);
+    return s;
+  }
+
+  // Probabilities of a tile: p_i = 2^(s_i * scale_log2 - m) in bf16, packed
+  // two per dword (pair k = elements 2k, 2k+1). Pair k's element i sits at
+  // key 8 (i / 4) + 4 g + i % 4 of the tile, which is the B-operand order of
+  // PV's 16-key step i / 8 with the keys' contraction order permuted.
+  static constexpr int EPC = 16 / NKC;  // exponentials per S MFMA
+  static_assert(EPC % 2 == 0, "whole pairs per MFMA");
+
+  // ---- phase 1: S(j+1) = K Q^T (NKC dependent MFMAs), each listed with EPC
+  // exponentials of tile j and the bf16 packing of the previous group's
+  // (the compiler's scheduler places them).
+  // The K operands are read two chunks ahead. Phase 2's V^T operands are read
+  // here too, half before the first MFMA and half after the second, so that
+  // at most 15 LDS reads are in flight (the wave's LDS counter) and the first
+  // MFMA waits for its own operand only.
+  static constexpr int NSTEP = 2 * NDB;
+  static __device__ __forceinline__ void s_phase(f32x16& snext, const uint8_t* kst, const bf16x8 (&qf)[NKC],
+                                                 const f32x16& scur, float scale_log2, float m, float (&e)[16],
+                                                 uint32_t (&pk)[8], int l32, int g, s16x8 (&va)[NSTEP],
+                                                 const uint8_t* vst, int v_row0, int v_col) {
+    bf16x8 ka[3];
+    ka[0] = read_k(kst, 0, l32, g);
+    if (NKC > 1) ka[1] = read_k(kst, 1, l32, g);
+#pragma unroll
+    for (int step = 0; step < NSTEP / 2; ++step) va[step] = read_v_step(vst, step, v_row0, v_col);
+    snext = f32x16{};
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      if (c + 2 < NKC) ka[(c + 2) % 3] = read_k(kst, c + 2, l32, g);
+      snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % 3], qf[c], snext, 0, 0, 0);
+#pragma unroll
+      for (int i = c * EPC; i < (c + 1) * EPC; ++i) e[i] = fast_exp2(fmaf(scur[i], scale_log2, -m));
+      if (c > 0) {
+#pragma unroll
+        for (int k = (c - 1) * EPC / 2; k < c * EPC / 2; ++k) pk[k] = pack_bf16(e[2 * k], e[2 * k + 1]);
+      }
+      if (c == (NKC > 1 ? 1 : 0)) {
+#pragma unroll
+        for (int step = NSTEP / 2; step < NSTEP; ++step) va[step] = read_v_step(vst, step, v_row0, v_col);
+      }
+      }
+    // consume the results in an empty asm: the compiler must compute them
+    // here, not sink them past the mask branch that follows into phase 2
+#pragma unroll
+    for (int k = 0; k < (NKC - 1) * EPC / 2; ++k) asm volatile("" : "+v"(pk[k]));
+#pragma unroll
+    for (int i = (NKC - 1) * EPC; i < 16; ++i) asm volatile("" : "+v"(e[i]));
+  }
+
+  static __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+
+  // ---- phase 2: O^T += V^T P^T (2 NDB MFMAs), each listed with the row-sum
+  // dot products of the probabilities and, from the third on, part of the
+  // row max of S(j+1). `va` holds every V^T operand (read in phase 1).
+  static __device__ __forceinline__ void pv_phase(f32x16 (&o)[NDB], const s16x8 (&va)[NSTEP], const float (&e)[16],
+                                                  uint32_t (&pk)[8], const f32x16& snext, float& mx, float& psum) {
+    constexpr int PPS = 8 / NSTEP;  // row-sum pairs per step
+    constexpr int MAX_FROM = NSTEP > 2 ? 2 : 0;  // S(j+1) is complete two MFMAs in
+    float part[2] = {0.0f, 0.0f};
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    // the 8 max3 operations of the tile's 16 scores, spread over steps MAX_FROM..
+    int nmax = 0;
 #pragma unroll
     for (int step = 0; step < NSTEP; ++step) {
-      if (step + 2 < NSTEP) va[(step + 2) % 3] = rd(step + 2);
+      if (step == 0) {
+        // the last group's pairs (not packed in phase 1)
+#pragma unroll
+        for (int k = (NKC - 1) * EPC / 2; k < 8; ++k) pk[k] = pack_bf16(e[2 * k], e[2 * k + 1]);
+      }
       const int kc = step / NDB, db = step % NDB;
+      const i32x4 b = {int(pk[4 * kc]), int(pk[4 * kc + 1]), int(pk[4 * kc + 2]), int(pk[4 * kc + 3])};
+      o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[step]),
+                                                      __builtin_bit_cast(bf16x8, b), o[db], 0, 0, 0);
 #pragma unroll
-      for (int h = 0; h < QB; ++h)
-        o[h][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[step % 3]), pb[h][kc],
-                                                           o[h][db], 0, 0, 0);
+      for (int k = step * PPS; k < (step + 1) * PPS; ++k) {
+        part[k % 2] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pk[k]), ones, part[k % 2], false);
+        asm volatile("" : "+v"(part[k % 2]));  // keep it next to this step's MFMA
+      }
+      if (step >= MAX_FROM) {
+        const int upto = 8 * (step + 1 - MAX_FROM) / (NSTEP - MAX_FROM);
 #pragma unroll
-      for (int e = 0; e < PER_STEP; ++e) {
-        const int idx = step * PER_STEP + e;  // element 1..15 of each block's max
-        if (idx < QB * 15) {
-          const int h = idx / 15, i = 1 + idx % 15;
-          mx[h] = fmaxf(mx[h], snext[h][i]);
+        for (; nmax < upto; ++nmax) {
+          if (nmax == 0)
+            mx = max3(snext[0], snext[1], snext[2]);
+          else if (nmax < 7)
+            mx = max3(mx, snext[2 * nmax + 1], snext[2 * nmax + 2]);
+          else
+            mx = __builtin_elementwise_maximum(mx, snext[15]);
         }
       }
-    }
-#pragma unroll
-    for (int h = 0; h < QB; ++h) mt[h] = half_swap_max(mx[h]) * scale_log2;
-  }
-
-  // ---- element mask: keys at or past a lane's limit get -inf
-  static __device__ __forceinline__ void mask(f32x16 (&s)[QB], int k0, int g, const int (&mylim)[QB]) {
-#pragma unroll
-    for (int h = 0; h < QB; ++h)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * (i / 4) + 4 * g + (i % 4);
-        if (key >= mylim[h]) s[h][i] = -INFINITY;
       }
+    psum = part[0] + part[1];
   }
 
-  // ---- tile max in log2 units per block, shared by both half-waves
-  static __device__ __forceinline__ void tile_max(const f32x16 (&s)[QB], float scale_log2, float (&mt)[QB]) {
+  // ---- element mask: keys at or past the lane's limit get -inf
+  static __device__ __forceinline__ void mask(f32x16& s, int k0, int g, int mylim) {
 #pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      float mx = s[h][0];
-#pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[h][i]);
-      mt[h] = half_swap_max(mx) * scale_log2;
+    for (int i = 0; i < 16; ++i) {
+      const int key = k0 + 8 * (i / 4) + 4 * g + (i % 4);
+      if (key >= mylim) s[i] = -INFINITY;
     }
   }
 
-  // ---- probabilities of a tile (bf16 B operands of PV) and their fp32 sums
-  static __device__ __forceinline__ void probs(const f32x16 (&s)[QB], float scale_log2, const RowState (&st)[QB],
-                                               bf16x8 (&pb)[QB][2], float (&psum)[QB]) {
+  // ---- tile max in log2 units, shared by both half-waves
+  static __device__ __forceinline__ float tile_max(const f32x16& s, float scale_log2) {
+    float mx = max3(s[0], s[1], s[2]);
 #pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      float part[2] = {0.0f, 0.0f};
-#pragma unroll
-      for (int i = 0; i < 16; ++i) pb[h][i / 8][i % 8] = (__bf16)fast_exp2(fmaf(s[h][i], scale_log2, -st[h].m));
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        const bf16x2 pair = {pb[h][i / 8][i % 8], pb[h][i / 8][i % 8 + 1]};
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-        part[(i / 2) % 2] = __builtin_amdgcn_fdot2_f32_bf16(pair, ones, part[(i / 2) % 2], false);
-      }
-      psum[h] = part[0] + part[1];
-    }
+    for (int i = 3; i < 15; i += 2) mx = max3(mx, s[i], s[i + 1]);
+    mx = __builtin_elementwise_maximum(mx, s[15]);
+    return half_swap_max(mx) * scale_log2;
   }
 };
 
 template <int D>
-__global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
-                                                          const __bf16* __restrict__ K,
-                                                          const __bf16* __restrict__ V,
-                                                          const int32_t* __restrict__ cu,
-                                                          const WorkItem* __restrict__ items, int H,
-                                                          float scale_log2, __bf16* __restrict__ O) {
+__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
+                                                                    const __bf16* __restrict__ K,
+                                                                    const __bf16* __restrict__ V,
+                                                                    const int32_t* __restrict__ cu,
+                                                                    const WorkItem* __restrict__ items, int H,
+                                                                    float scale_log2, __bf16* __restrict__ O) {
   using Kn = Kernel<D>;
   using Cfg = typename Kn::Cfg;
   using s16x8 = typename Kn::s16x8;
-  constexpr int BN = Cfg::BN, QB = Cfg::QB, NKC = Cfg::NKC, NDB = Cfg::NDB, NS = Cfg::NS;
+  constexpr int BN = Cfg::BN, NKC = Cfg::NKC, NDB = Cfg::NDB, NS = Cfg::NS;
   static_assert(NS == 4, "the loop below is unrolled for a ring of four stages");
   // separate arrays per stage: the compiler sees that an LDS DMA into one
   // stage and reads of another do not alias
@@ -329,15 +262,11 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + base);
 
-  // this lane's query rows (one per block) and their key limits; rows past
-  // the sequence end act as image rows (their outputs are never stored)
-  const int wrow0 = it.q0 + 32 * QB * wave;
-  int qrow[QB], mylim[QB];
-#pragma unroll
-  for (int h = 0; h < QB; ++h) {
-    qrow[h] = wrow0 + 32 * h + l32;
-    mylim[h] = key_limit(qrow[h], T, L);
-  }
+  // this lane's query row and its key limit; rows past the sequence end act
+  // as image rows (their outputs are never stored)
+  const int wrow0 = it.q0 + 32 * wave;
+  const int qrow = wrow0 + l32;
+  const int mylim = key_limit(qrow, T, L);
   const int wlim_min = key_limit(wrow0, T, L);  // smallest key limit of the wave's rows
   const int kend = it.k_end;
 
@@ -365,26 +294,20 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   if (kend > 3) ld_k(3, kst[3]);
   if (kend > 2) ld_v(2, vst[2]);
 
-  // Q^T operands: chunk c holds d = 16c + 8g .. +7 of this lane's query rows
-  bf16x8 qf[QB][NKC];
+  // Q^T operands: chunk c holds d = 16c + 8g .. +7 of this lane's query row
+  bf16x8 qf[NKC];
 #pragma unroll
-  for (int h = 0; h < QB; ++h)
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) {
-      if (qrow[h] < L)
-        qf[h][c] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(qrow[h]) * rs + 16 * c + 8 * g);
-      else
-        qf[h][c] = bf16x8{};
-    }
+  for (int c = 0; c < NKC; ++c) {
+    if (qrow < L)
+      qf[c] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(qrow) * rs + 16 * c + 8 * g);
+    else
+      qf[c] = bf16x8{};
+  }
 
-  f32x16 oacc[QB][NDB];
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int h = 0; h < QB; ++h)
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) oacc[h][db] = f32x16{};
-  RowState st[QB];
-#pragma unroll
-  for (int h = 0; h < QB; ++h) st[h] = RowState{-INFINITY, 0.0f};
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  RowState st{-INFINITY, 0.0f};
 
   // per-lane constant parts of the V^T (transpose-read) addresses
   const int v_row0 = 4 * g + (lane & 15) / 4;
@@ -397,59 +320,47 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
     wait_vmcnt<0>();
   lds_barrier();
 
-  f32x16 sa[QB], sb[QB];
+  f32x16 sa, sb;
   // S(0) and its reference max. Rows past the sequence end, and tiles past a
   // row's key limit, are computed masked: their probabilities are exactly
   // zero. That keeps every branch in the loop scalar and rare.
   if (kend > 0) {
-    bf16x8 ka[NKC];
-    Kn::read_k(ka, kst[0], l32, g);
-    Kn::s_mfma(sa, ka, qf);
+    sa = Kn::s_tile(kst[0], qf, l32, g);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
-    float mt[QB];
-    Kn::tile_max(sa, scale_log2, mt);
-#pragma unroll
-    for (int h = 0; h < QB; ++h) st[h].m = mt[h];  // first tile: O and l are still zero
+    st.m = Kn::tile_max(sa, scale_log2);  // first tile: O and l are still zero
   }
 
-  // Iteration j; `scur` holds S(j), `snext`
-  // receives S(j+1). SJ = j % NS (compile-time in each unrolled copy). The
-  // rare branches (element mask, rescale) are marked unlikely so that the
-  // common path falls through without a taken branch.
-  auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[QB], f32x16(&snext)[QB]) {
+  // Iteration j; `scur` holds S(j), `snext` receives S(j+1). SJ = j % NS
+  // (compile-time in each unrolled copy). The rare branches (element mask,
+  // rescale) are marked unlikely so that the common path falls through.
+  auto iteration = [&](auto sj_tag, int j, f32x16& scur, f32x16& snext) {
     constexpr int SJ = decltype(sj_tag)::value;
     lds_barrier();  // every wave is done with S(j) (K stage SJ) and PV(j-1) (V stage SJ-1)
     const bool steady = j + NS < kend;
     if (steady) ld_k(j + NS, kst[SJ]);
     if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
     const int k1 = (j + 1) * BN;
-    // the first two V^T operands of PV(j): their LDS latency hides behind block A
-    const s16x8 va0 = Kn::read_v_step(vst[SJ], 0, v_row0, v_col);
-    const s16x8 va1 = Kn::read_v_step(vst[SJ], 1, v_row0, v_col);
-    // S(j+1) MFMAs interleaved with the exponentials of tile j
-    bf16x8 pb[QB][2];
-    float psum[QB];
-    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st, pb, psum, l32, g);
-#pragma unroll
-    for (int h = 0; h < QB; ++h) st[h].l += psum[h];
+    s16x8 va[Kn::NSTEP];  // V^T operands of PV(j), read during phase 1
+    float e[16];
+    uint32_t pk[8];
+    Kn::s_phase(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st.m, e, pk, l32, g, va, vst[SJ], v_row0,
+                v_col);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
-    // PV(j) MFMAs interleaved with the row max of tile j+1
-    float mt[QB];
-    Kn::pv_with_max(oacc, vst[SJ], pb, snext, scale_log2, mt, v_row0, v_col, va0, va1);
+    float mx, psum;
+    Kn::pv_phase(oacc, va, e, pk, snext, mx, psum);
+    st.l += psum;
+    const float mt = half_swap_max(mx) * scale_log2;
+    const bool need = mt > st.m + kLazyRescale;
+    if (__builtin_expect(wave_any(need), 0)) {
+      // per-lane decision: a lane that does not need it keeps its max (alpha = 1
+      // exactly), so each row's arithmetic depends on its own scores only
+      const float alpha = need ? fast_exp2(st.m - mt) : 1.0f;
 #pragma unroll
-    for (int h = 0; h < QB; ++h) {
-      const bool need = mt[h] > st[h].m + kLazyRescale;
-      if (__builtin_expect(wave_any(need), 0)) {
-        // per-lane decision: a lane that does not need it keeps its max (alpha = 1
-        // exactly), so each row's arithmetic depends on its own scores only
-        const float alpha = need ? fast_exp2(st[h].m - mt[h]) : 1.0f;
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[h][db][i] *= alpha;
-        st[h].l *= alpha;
-        st[h].m = need ? mt[h] : st[h].m;
-      }
+        for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+      st.l *= alpha;
+      st.m = need ? mt : st.m;
     }
     // K(j+2) and V(j+1) are needed next; the loads of iterations j-1 and j
     // may stay in flight in steady state
@@ -477,22 +388,19 @@ __global__ __launch_bounds__(kBf16BlockM * 2 / PVA_BF16_QB, 3 - PVA_BF16_QB) voi
   }
 
   // ---- epilogue: O = O^T / l, bf16, rows of this sequence only
+  const float lt = half_swap_sum(st.l);
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
+  if (qrow < L) {
+    __bf16* orow = O + base + int64_t(qrow) * rs;
 #pragma unroll
-  for (int h = 0; h < QB; ++h) {
-    const float lt = half_swap_sum(st[h].l);
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-    if (qrow[h] < L) {
-      __bf16* orow = O + base + int64_t(qrow[h]) * rs;
+    for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int db = 0; db < NDB; ++db)
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
 #pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[h][db][4 * i4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * i4 + 4 * g) = w;
-        }
-    }
+        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][4 * i4 + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * i4 + 4 * g) = w;
+      }
   }
 }
 

@@ -26,9 +26,10 @@ constexpr float kLazyRescale = 8.0f;
 
 // Maximum over the two 32-lane halves of a wave: permlane32_swap(x, x) hands
 // each lane its own value and its partner's (lane ^ 32) in some order.
+// (IEEE maximum: no canonicalisation of the MFMA results it reads)
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return __builtin_elementwise_maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
