@@ -16,17 +16,25 @@ Pins (all in tests/test_oracle.py, run without a GPU):
   * closed forms (row 0 equals v0; K = 0 gives running means);
   * the textbook extremes (no text: plain attention; no image: causal);
   * hand-derived golden values under tests/golden/;
-  * the e4m3 table against the format's defining values and torch's cast.
+  * the e4m3 table against the format's defining values and torch's cast;
+  * multi-segment masks (``oracle.segments``): the two-segment case equals the
+    mixed mask, a hand-written golden mask, brute force through a second
+    characterisation of the allowed keys, suffix-query consistency and
+    invariance under permutations inside an image block (tests/test_oracle_segments.py).
 Nothing is "parity unpinned".
 """
 from .attention import (mixed_mask, masked_softmax, masked_attention, attention_probs,
                         packed_attention, packed_attention_rows, padded_layout, padded_mask,
                         padded_attention, unpad, useful_flops, offsets)
-from .brute import brute_packed_attention, allowed_keys
+from .brute import brute_packed_attention, allowed_keys, brute_segment_attention, segment_allowed_keys
+from .segments import (CAUSAL, FULL, SegSeq, make_seq, segment_mask, segment_attention,
+                       segment_attention_rows, segment_useful_flops)
 from . import fp8
 
 __all__ = [
     "mixed_mask", "masked_softmax", "masked_attention", "attention_probs", "packed_attention",
     "packed_attention_rows", "padded_layout", "padded_mask", "padded_attention", "unpad",
     "useful_flops", "offsets", "brute_packed_attention", "allowed_keys", "fp8",
+    "brute_segment_attention", "segment_allowed_keys", "CAUSAL", "FULL", "SegSeq", "make_seq",
+    "segment_mask", "segment_attention", "segment_attention_rows", "segment_useful_flops",
 ]

@@ -141,3 +141,82 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
     except Exception:
         ok = False  # a crash also counts as caught
     assert not ok, f"mutant {name} slipped through every pin"
+
+
+# ---- the multi-segment oracle: its own pins (golden masks, brute force
+# through the second characterisation, agreement with the two-segment mask)
+import oracle.segments as osg  # noqa: E402
+
+
+def _segment_pins_pass():
+    with open(os.path.join(GOLDEN, "hand_segment_masks.json")) as f:
+        g = json.load(f)
+    for case in g["cases"]:
+        if not np.array_equal(osg.segment_mask(case["seg_len"], case["seg_kind"]).astype(int), np.array(case["mask"])):
+            return False
+    for T, I in ((3, 4), (0, 5), (6, 0)):
+        if not np.array_equal(osg.segment_mask([T, I], [0, 1]), oracle.mixed_mask(T, T + I)):
+            return False
+    rng = np.random.default_rng(500)
+    seqs = [osg.make_seq([2, 3, 1, 2], [0, 1, 0, 1], 1), osg.make_seq([3, 2], [1, 0], 0)]
+    Nk = sum(s.length for s in seqs)
+    Nq = sum(s.q_rows for s in seqs)
+    k, v = (rng.standard_normal((Nk, 1, 3)) for _ in range(2))
+    q = rng.standard_normal((Nq, 1, 3))
+    ref = osg.segment_attention(q, k, v, seqs, 0.7)
+    bo = np.array(oracle.brute_segment_attention(q.tolist(), k.tolist(), v.tolist(), seqs, 0.7)).reshape(ref.shape)
+    return np.max(np.abs(bo - ref)) < 1e-12
+
+
+def _seg_full_block_causal(seg_len, seg_kind):
+    return _SEG_ORIG(seg_len, [0] * len(seg_kind))
+
+
+def _seg_full_block_misses_prefix(seg_len, seg_kind):
+    m = _SEG_ORIG(seg_len, seg_kind)
+    a = 0
+    for n, kind in zip(seg_len, seg_kind):
+        if kind == 1:
+            m[a:a + n, :a] = False
+        a += n
+    return m
+
+
+def _seg_causal_sees_own_segment(seg_len, seg_kind):
+    m = _SEG_ORIG(seg_len, seg_kind)
+    a = 0
+    for n, kind in zip(seg_len, seg_kind):
+        if kind == 0:
+            m[a:a + n, :a + n] = True
+        a += n
+    return m
+
+
+def _seg_block_end_off_by_one(seg_len, seg_kind):
+    m = _SEG_ORIG(seg_len, seg_kind)
+    a = 0
+    for n, kind in zip(seg_len, seg_kind):
+        if kind == 1 and n > 1:
+            m[a:a + n, a + n - 1] = False
+        a += n
+    return m
+
+
+_SEG_ORIG = osg.segment_mask
+SEG_MUTANTS = {
+    "full_block_causal": _seg_full_block_causal,
+    "full_block_misses_prefix": _seg_full_block_misses_prefix,
+    "causal_sees_own_segment": _seg_causal_sees_own_segment,
+    "block_end_off_by_one": _seg_block_end_off_by_one,
+}
+
+
+def test_unmutated_segment_oracle_passes():
+    assert _segment_pins_pass()
+
+
+@pytest.mark.parametrize("name", sorted(SEG_MUTANTS))
+def test_segment_pins_catch_planted_mistake(name, monkeypatch):
+    monkeypatch.setattr(osg, "segment_mask", SEG_MUTANTS[name])
+    ok = _segment_pins_pass()  # a mutant must fail a pin, not crash
+    assert not ok, f"mutant {name} slipped through every pin"
