@@ -129,11 +129,13 @@ def pmc_summary(args):
 
 def algorithmic_bytes(w):
     """Q, K, V read once and O written once (fp8: 1-byte inputs, bf16 output),
-    plus the per-(sequence, head) scales of the fp8 path."""
-    n_el = w.total_tokens * w.num_heads * w.head_dim
+    plus the per-(sequence, head) scales of the fp8 path. Q and O hold the
+    queried rows, K and V every token."""
+    nq = w.total_q if isinstance(w, workloads.SegWorkload) else w.total_tokens
+    hd = w.num_heads * w.head_dim
     if w.dtype == "fp8":
-        return 3 * n_el + 2 * n_el + 3 * 4 * w.nseq * w.num_heads
-    return 4 * 2 * n_el
+        return nq * hd + 2 * w.total_tokens * hd + 2 * nq * hd + 3 * 4 * w.nseq * w.num_heads
+    return 2 * (2 * nq * hd + 2 * w.total_tokens * hd)
 
 
 def stored_traffic(dtype, workload):
@@ -190,35 +192,49 @@ def main():
         return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]()
+    segmented = isinstance(w, workloads.SegWorkload)
     is_fp8 = w.dtype == "fp8"
     dtype = "fp8" if is_fp8 else "bf16"
     H, D = w.num_heads, w.head_dim
     scale = 1.0 / math.sqrt(D)
-    log(f"[bench] workload {w.name}: T={w.text_len} I={w.image_len} N={w.total_tokens} H={H} D={D} {dtype}")
+    if segmented:
+        log(f"[bench] workload {w.name}: {w.nseq} sequences, Nk={w.total_tokens} Nq={w.total_q} H={H} D={D} {dtype}")
+    else:
+        log(f"[bench] workload {w.name}: T={w.text_len} I={w.image_len} N={w.total_tokens} H={H} D={D} {dtype}")
+    n_q = w.total_q if segmented else w.total_tokens
 
     # ---------------- inputs (seeded, synthetic), resident in HBM
     t0 = time.time()
+    qs = ks = vs = None
     if is_fp8:
-        q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+        q8, k8, v8, qs, ks, vs = workloads.seg_fp8_inputs(w) if segmented else workloads.fp8_inputs(w)
         q, k, v = (x.view(torch.uint8).to(dev) for x in (q8, k8, v8))
         qsd, ksd, vsd = (torch.from_numpy(x).to(dev) for x in (qs, ks, vs))
     else:
-        qc, kc, vc = workloads.bf16_inputs(w)
+        qc, kc, vc = workloads.seg_bf16_inputs(w) if segmented else workloads.bf16_inputs(w)
         q, k, v = (x.to(dev) for x in (qc, kc, vc))
-    out = torch.empty((w.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((n_q, H, D), dtype=torch.bfloat16, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs ready in {time.time() - t0:.1f}s")
 
     # ---------------- descriptor (built once per batch composition)
     t0 = time.perf_counter()
-    desc = pva.SegDesc(w.text_len, w.image_len, H, D, dtype)
+    if segmented:
+        desc = pva.SegDesc.segments(w.seqs, H, D, dtype)
+    else:
+        desc = pva.SegDesc(w.text_len, w.image_len, H, D, dtype)
     desc_us = (time.perf_counter() - t0) * 1e6
     cu = torch.from_numpy(desc.cu_seqlens).to(dev)
+    cuq = torch.from_numpy(desc.cu_seqlens_q).to(dev)
     flops = desc.useful_flops
     stream = torch.cuda.current_stream()
 
     def step():
-        if is_fp8:
+        if segmented and is_fp8:
+            pva.packed_attn_fwd_varlen_fp8(q, k, v, qsd, ksd, vsd, cuq, cu, desc, scale, out, stream)
+        elif segmented:
+            pva.packed_attn_fwd_varlen(q, k, v, cuq, cu, desc, scale, out, stream)
+        elif is_fp8:
             pva.packed_attn_fwd_fp8(q, k, v, qsd, ksd, vsd, cu, desc, scale, out, stream)
         else:
             pva.packed_attn_fwd(q, k, v, cu, desc, scale, out, stream)
@@ -260,8 +276,8 @@ def main():
         "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
         "config": {
             "workload": w.name,
-            "text_len": list(w.text_len),
-            "image_len": list(w.image_len),
+            **({"segments": [[list(a), list(b), int(c)] for a, b, c in w.seqs], "queried_rows": w.total_q}
+               if segmented else {"text_len": list(w.text_len), "image_len": list(w.image_len)}),
             "total_tokens": w.total_tokens,
             "num_heads": H,
             "head_dim": D,
@@ -310,7 +326,7 @@ def main():
         log(f"[bench] cold median {cmed:.4f} ms -> {result['cold']['tflops']} TFLOP/s")
 
     # ---------------- padded-mask baseline: pad to Lmax + explicit (B,1,Lmax,Lmax) bool mask + SDPA
-    if not args.no_padded and not is_fp8:
+    if not args.no_padded and not is_fp8 and not segmented:
         result["padded_sdpa"] = padded_baseline(w, q, k, v, scale, args.padded_steps, flops, ms_per_step)
     torch.cuda.synchronize()
 
@@ -389,27 +405,38 @@ def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales):
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
     except Exception:
         threads = os.cpu_count() or 1
+    segmented = isinstance(w, workloads.SegWorkload)
+    q_rows = w.q_rows if segmented else w.seq_len
     qn, kn, vn = (x.cpu() for x in (q, k, v))
     if is_fp8:
         qs, ks, vs = fp8_scales
-        qn, kn, vn = (oracle.fp8.dequantize(x.numpy(), s, w.seq_len) for x, s in ((qn, qs), (kn, ks), (vn, vs)))
+        qn = oracle.fp8.dequantize(qn.numpy(), qs, q_rows)
+        kn, vn = (oracle.fp8.dequantize(x.numpy(), s, w.seq_len) for x, s in ((kn, ks), (vn, vs)))
     else:
         qn, kn, vn = (x.float().numpy() for x in (qn, kn, vn))
     got = out.float().cpu().numpy()
-    off = oracle.offsets(w.seq_len)
+    koff = oracle.offsets(w.seq_len)
+    qoff = oracle.offsets(q_rows)
     # a fixed order over (sequence, head): every sequence, head 0 first, then head 1, ...
     order = [(s, h) for h in range(w.num_heads) for s in range(w.nseq)]
     done_flops, t_used, n = 0, 0.0, 0
     worst, total, cnt = 0.0, 0.0, 0
     for s, h in order:
-        a, b = off[s], off[s + 1]
-        T, I = w.text_len[s], w.image_len[s]
+        a, b, qa, qb = koff[s], koff[s + 1], qoff[s], qoff[s + 1]
+        if qb == qa:
+            continue
         t0 = time.perf_counter()
-        ref = oracle.masked_attention(qn[a:b, h], kn[a:b, h], vn[a:b, h], oracle.mixed_mask(T, T + I), scale)
+        if segmented:
+            seq = oracle.make_seq(*w.seqs[s])
+            mask = oracle.segment_mask(seq.seg_len, seq.seg_kind)[seq.q_start:]
+        else:
+            T, I = w.text_len[s], w.image_len[s]
+            mask = oracle.mixed_mask(T, T + I)
+        ref = oracle.masked_attention(qn[qa:qb, h], kn[a:b, h], vn[a:b, h], mask, scale)
         t_used += time.perf_counter() - t0
-        done_flops += oracle.useful_flops([T], [I], 1, w.head_dim)
+        done_flops += 4 * w.head_dim * int(mask.sum())
         n += 1
-        d = np.abs(got[a:b, h].astype(np.float64) - ref)
+        d = np.abs(got[qa:qb, h].astype(np.float64) - ref)
         worst = max(worst, float(d.max()))
         total += float(d.sum())
         cnt += d.size

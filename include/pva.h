@@ -22,6 +22,10 @@
  * Layout: Q, K, V and O are [N, H, D] row-major (D contiguous), N = sum L_s,
  * in pack order. All heads share one sequence structure (no GQA).
  *
+ * Generalization (pva_seg_desc_build_segments): a sequence may be any list of
+ * text (causal) and image (full) segments, and only a suffix of it may be
+ * queried, with Q and O holding just the queried rows.
+ *
  * Ownership: the caller owns every tensor and every stream. The library owns
  * only a pva_seg_desc (host copy + device work list), freed by
  * pva_seg_desc_free. No call allocates device memory except
@@ -51,6 +55,14 @@ typedef enum {
 } pva_status;
 
 typedef enum { PVA_BF16 = 0, PVA_FP8_E4M3 = 1 } pva_dtype;
+
+/* Segment kinds of the multi-segment Generalized Causal mask ("[RFC]:
+ * HunyuanImage 3.0 deployment", Model structure item 1, which interleaves
+ * text and image segments in one context): a token of a CAUSAL (text)
+ * segment at position i sees keys 0..i of its sequence; a token of a FULL
+ * (image) block [a, b) sees keys 0..b-1 (every earlier segment and its whole
+ * block). */
+typedef enum { PVA_SEG_CAUSAL = 0, PVA_SEG_FULL = 1 } pva_seg_kind;
 
 /* Opaque, library-owned descriptor of one batch composition. */
 typedef struct pva_seg_desc pva_seg_desc;
@@ -89,20 +101,65 @@ int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, i
                             int32_t num_heads, int32_t head_dim, pva_dtype dtype,
                             pva_seg_desc** out);
 
-/* Host view of the descriptor's cu_seqlens (int32 [nseq + 1]); valid until
- * the descriptor is freed. */
+/*
+ * General builder: any number of segments per sequence (the multi-segment
+ * Generalized Causal mask above), and optionally only a suffix of each
+ * sequence queried. Queries then cover rows [q_start_s, L_s) of sequence s:
+ * K and V still hold all L_s rows (a prefix computed once and reused, the
+ * RFC's single "Prefix KV", Model structure item 1), while Q and O hold only
+ * the queried rows, packed in sequence order (cu_seqlens_q below).
+ *
+ *   seg_len, seg_kind : host int32, all sequences' segments back to back
+ *                       (sum of seg_count entries); lengths >= 0, kinds
+ *                       PVA_SEG_CAUSAL or PVA_SEG_FULL; every sequence needs
+ *                       at least one token
+ *   seg_count         : host int32 [nseq], segments per sequence (>= 1)
+ *   q_start           : host int32 [nseq] in [0, L_s], or NULL for all zero
+ *   others            : as pva_seg_desc_build
+ * (text_len, image_len) of pva_seg_desc_build is the case of two segments
+ * {CAUSAL T_s, FULL I_s} with q_start = 0. A descriptor with any q_start > 0
+ * is launched with packed_attn_fwd_varlen / _varlen_fp8 only.
+ */
+int pva_seg_desc_build_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                                pva_dtype dtype, void* stream, pva_seg_desc** out);
+
+/* Host-only planning of the general builder (inspection, no device). */
+int pva_seg_desc_build_segments_host(const int32_t* seg_len, const int32_t* seg_kind,
+                                     const int32_t* seg_count, const int32_t* q_start, int32_t nseq,
+                                     int32_t num_heads, int32_t head_dim, pva_dtype dtype,
+                                     pva_seg_desc** out);
+
+/* Host view of the descriptor's cu_seqlens (int32 [nseq + 1], offsets of the
+ * sequences' K/V rows); valid until the descriptor is freed. */
 int pva_seg_desc_cu_seqlens(const pva_seg_desc* desc, const int32_t** host_cu, int32_t* len);
 
-/* Useful multiply-add FLOPs over allowed (query, key) pairs only:
- * 4 * D * H * sum_s [T_s (T_s + 1) / 2 + I_s * L_s]. Returns -1 on NULL. */
+/* Host view of the query-row offsets (int32 [nseq + 1]): cu_seqlens_q[s]
+ * is the first Q/O row of sequence s. Equal to cu_seqlens when every
+ * q_start is 0. Valid until freed. */
+int pva_seg_desc_cu_seqlens_q(const pva_seg_desc* desc, const int32_t** host_cu_q, int32_t* len);
+
+/* Host view of the per-token key limits (int32 [N]): row i of sequence s
+ * may attend to keys [0, lim) of that sequence, lim = key_limits[
+ * cu_seqlens[s] + i]. Non-decreasing within a sequence. Valid until freed. */
+int pva_seg_desc_key_limits(const pva_seg_desc* desc, const int32_t** key_limits, int32_t* len);
+
+/* Useful multiply-add FLOPs over allowed (query, key) pairs of the queried
+ * rows only: 4 * D * H * sum over queried rows of lim; for two segments and
+ * q_start = 0 that is 4 * D * H * sum_s [T_s (T_s + 1) / 2 + I_s * L_s].
+ * Returns -1 on NULL. */
 int64_t pva_seg_desc_useful_flops(const pva_seg_desc* desc);
 
 /* Tile shape the descriptor was planned with (query rows BM, keys BN). */
 int pva_seg_desc_tile(const pva_seg_desc* desc, int32_t* block_m, int32_t* block_n);
 
 /* Host view of the work list in launch order: int32 [n_items][8] records
- * {seq, head, q0, q_rows, k_full_end, k_end, T, L}; seq = -1 marks an empty
- * slot that keeps the XCD alignment of the list. Valid until freed. */
+ * {seq, head, q0, q_rows, k_full_end, k_end, qo_row, L}: query rows
+ * [q0, q0 + q_rows) of sequence seq (row numbers within the sequence), key
+ * tiles below k_full_end need no mask, tiles from k_end on are skipped,
+ * qo_row is the Q/O row holding query row q0, L the sequence length;
+ * seq = -1 marks an empty slot that keeps the XCD alignment of the list.
+ * Valid until freed. */
 int pva_seg_desc_work_items(const pva_seg_desc* desc, const int32_t** items, int32_t* n_items);
 
 /* Free a descriptor (NULL is a no-op). Releases its device work list with
@@ -119,6 +176,8 @@ void pva_seg_desc_free(pva_seg_desc* desc);
  *   out        : device bf16 [N, H, D], 16-byte aligned; every row of every
  *                sequence is written; nothing outside [N, H, D] is touched
  *   stream     : hipStream_t to launch on (NULL = null stream)
+ * The descriptor may come from either builder as long as every q_start is 0
+ * (else PVA_ERR_INVALID_ARG: use packed_attn_fwd_varlen).
  * Asynchronous; allocates nothing. With the environment variable PVA_CHECK=1
  * the device cu_seqlens is copied back (synchronously) and compared with the
  * descriptor's before the launch.
@@ -138,6 +197,24 @@ int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
 int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                         const float* k_scale, const float* v_scale, const int32_t* cu_seqlens,
                         const pva_seg_desc* seg_desc, float scale, void* out, void* stream);
+
+/*
+ * Forward over a descriptor from pva_seg_desc_build_segments (or any other):
+ * q and out hold the queried rows only ([cu_seqlens_q[nseq], H, D]), k and v
+ * whole sequences ([cu_seqlens[nseq], H, D]). cu_seqlens_q / cu_seqlens_k
+ * are device int32 [nseq + 1] equal to the descriptor's (checked with
+ * PVA_CHECK=1). Every queried row is written; nothing else in out is
+ * touched. Otherwise as packed_attn_fwd.
+ */
+int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
+                           void* stream);
+
+/* FP8 variant of packed_attn_fwd_varlen (scales as in packed_attn_fwd_fp8). */
+int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                               const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                               void* out, void* stream);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* pva_last_error(void);

@@ -24,11 +24,15 @@ PVA_ERR_UNSUPPORTED = -2
 PVA_ERR_HIP = -3
 PVA_ERR_NO_MEMORY = -4
 DTYPES = {"bf16": 0, "fp8": 1}
+SEG_CAUSAL = 0  # text segment: a token sees every key up to itself
+SEG_FULL = 1    # image block: a token sees every key up to the end of its block
 
 EXPORTED = [
-    "pva_seg_desc_build", "pva_seg_desc_build_host", "pva_seg_desc_cu_seqlens", "pva_seg_desc_useful_flops",
-    "pva_seg_desc_tile", "pva_seg_desc_work_items", "pva_seg_desc_free", "packed_attn_fwd",
-    "packed_attn_fwd_fp8", "pva_last_error", "pva_version",
+    "pva_seg_desc_build", "pva_seg_desc_build_host", "pva_seg_desc_build_segments",
+    "pva_seg_desc_build_segments_host", "pva_seg_desc_cu_seqlens", "pva_seg_desc_cu_seqlens_q",
+    "pva_seg_desc_key_limits", "pva_seg_desc_useful_flops", "pva_seg_desc_tile", "pva_seg_desc_work_items",
+    "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
+    "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version",
 ]
 
 
@@ -58,6 +62,16 @@ def lib() -> ctypes.CDLL:
     L.pva_seg_desc_build_host.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int, ctypes.POINTER(vp)]
     L.pva_seg_desc_build_host.restype = ctypes.c_int
+    L.pva_seg_desc_build_segments.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build_segments.restype = ctypes.c_int
+    L.pva_seg_desc_build_segments_host.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build_segments_host.restype = ctypes.c_int
+    L.pva_seg_desc_cu_seqlens_q.argtypes = [vp, ctypes.POINTER(i32p), i32p]
+    L.pva_seg_desc_cu_seqlens_q.restype = ctypes.c_int
+    L.pva_seg_desc_key_limits.argtypes = [vp, ctypes.POINTER(i32p), i32p]
+    L.pva_seg_desc_key_limits.restype = ctypes.c_int
     L.pva_seg_desc_cu_seqlens.argtypes = [vp, ctypes.POINTER(i32p), i32p]
     L.pva_seg_desc_cu_seqlens.restype = ctypes.c_int
     L.pva_seg_desc_useful_flops.argtypes = [vp]
@@ -72,6 +86,10 @@ def lib() -> ctypes.CDLL:
     L.packed_attn_fwd.restype = ctypes.c_int
     L.packed_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
     L.packed_attn_fwd_fp8.restype = ctypes.c_int
+    L.packed_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    L.packed_attn_fwd_varlen.restype = ctypes.c_int
+    L.packed_attn_fwd_varlen_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
+    L.packed_attn_fwd_varlen_fp8.restype = ctypes.c_int
     L.pva_last_error.argtypes = []
     L.pva_last_error.restype = ctypes.c_char_p
     L.pva_version.argtypes = []
@@ -130,10 +148,56 @@ class SegDesc:
         self._h = h
         self.text_len = tuple(int(x) for x in t_arr)
         self.image_len = tuple(int(x) for x in i_arr)
+        self._nseq = len(t_arr)
         self.num_heads = int(num_heads)
         self.head_dim = int(head_dim)
         self.dtype = dtype
         self.host_only = host_only
+
+    @classmethod
+    def segments(cls, seqs, num_heads: int, head_dim: int, dtype: str = "bf16", stream=None,
+                 host_only: bool = False) -> "SegDesc":
+        """General descriptor. ``seqs``: one entry per sequence, each
+        ``(seg_len, seg_kind)`` or ``(seg_len, seg_kind, q_start)`` with kinds
+        SEG_CAUSAL / SEG_FULL (objects with those attributes work too)."""
+        if dtype not in DTYPES:
+            raise PvaError(PVA_ERR_INVALID_ARG, f"dtype must be one of {sorted(DTYPES)}")
+        lens, kinds, counts, starts = [], [], [], []
+        for sq in seqs:
+            if hasattr(sq, "seg_len"):
+                sl, sk, qs = sq.seg_len, sq.seg_kind, getattr(sq, "q_start", 0)
+            else:
+                sl, sk = sq[0], sq[1]
+                qs = sq[2] if len(sq) > 2 else 0
+            if len(sl) != len(sk):
+                raise PvaError(PVA_ERR_INVALID_ARG, "one kind per segment")
+            lens += list(sl)
+            kinds += list(sk)
+            counts.append(len(sl))
+            starts.append(qs)
+        L = lib()
+        la, lp = _i32_array(lens if lens else [0])
+        ka, kp = _i32_array(kinds if kinds else [0])
+        ca, cp = _i32_array(counts)
+        sa, sp = _i32_array(starts)
+        h = ctypes.c_void_p()
+        if host_only:
+            st = L.pva_seg_desc_build_segments_host(lp, kp, cp, sp, len(ca), int(num_heads), int(head_dim),
+                                                    DTYPES[dtype], ctypes.byref(h))
+        else:
+            st = L.pva_seg_desc_build_segments(lp, kp, cp, sp, len(ca), int(num_heads), int(head_dim),
+                                               DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream)),
+                                               ctypes.byref(h))
+        _check(st)
+        self = cls.__new__(cls)
+        self._h = h
+        self.text_len = self.image_len = None
+        self._nseq = len(ca)
+        self.num_heads = int(num_heads)
+        self.head_dim = int(head_dim)
+        self.dtype = dtype
+        self.host_only = host_only
+        return self
 
     @property
     def handle(self) -> ctypes.c_void_p:
@@ -143,7 +207,7 @@ class SegDesc:
 
     @property
     def nseq(self) -> int:
-        return len(self.text_len)
+        return self._nseq
 
     @property
     def cu_seqlens(self) -> np.ndarray:
@@ -157,6 +221,24 @@ class SegDesc:
         return int(self.cu_seqlens[-1])
 
     @property
+    def cu_seqlens_q(self) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        _check(lib().pva_seg_desc_cu_seqlens_q(self.handle, ctypes.byref(p), ctypes.byref(n)))
+        return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
+
+    @property
+    def total_q(self) -> int:
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def key_limits(self) -> np.ndarray:
+        p = ctypes.POINTER(ctypes.c_int32)()
+        n = ctypes.c_int32()
+        _check(lib().pva_seg_desc_key_limits(self.handle, ctypes.byref(p), ctypes.byref(n)))
+        return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
+
+    @property
     def useful_flops(self) -> int:
         return int(lib().pva_seg_desc_useful_flops(self.handle))
 
@@ -168,7 +250,7 @@ class SegDesc:
 
     @property
     def work_items(self) -> np.ndarray:
-        """int32 [n_items, 8]: seq, head, q0, q_rows, k_full_end, k_end, T, L (launch order)."""
+        """int32 [n_items, 8]: seq, head, q0, q_rows, k_full_end, k_end, qo_row, L (launch order)."""
         p = ctypes.POINTER(ctypes.c_int32)()
         n = ctypes.c_int32()
         _check(lib().pva_seg_desc_work_items(self.handle, ctypes.byref(p), ctypes.byref(n)))
@@ -194,22 +276,32 @@ def _ptr(t) -> ctypes.c_void_p:
 
 def _check_qkvo(desc: SegDesc, tensors, elt_dtypes, out) -> None:
     import torch
-    N, H, D = desc.total_tokens, desc.num_heads, desc.head_dim
+    Nk, Nq, H, D = desc.total_tokens, desc.total_q, desc.num_heads, desc.head_dim
     for name, t in tensors:
+        N = Nq if name == "q" else Nk
         if not isinstance(t, torch.Tensor) or not t.is_cuda:
             raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a device tensor")
         if t.dtype not in elt_dtypes:
             raise PvaError(PVA_ERR_INVALID_ARG, f"{name} has dtype {t.dtype}, expected one of {elt_dtypes}")
         if tuple(t.shape) != (N, H, D) or not t.is_contiguous():
             raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be contiguous [{N}, {H}, {D}], got {tuple(t.shape)}")
-    if not out.is_cuda or out.dtype != torch.bfloat16 or tuple(out.shape) != (N, H, D) or not out.is_contiguous():
-        raise PvaError(PVA_ERR_INVALID_ARG, f"out must be a contiguous device bf16 [{N}, {H}, {D}] tensor")
+    if (not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.bfloat16
+            or tuple(out.shape) != (Nq, H, D) or not out.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out must be a contiguous device bf16 [{Nq}, {H}, {D}] tensor")
 
 
-def _check_cu(desc: SegDesc, cu) -> None:
+def _check_cu(desc: SegDesc, cu, name: str = "cu_seqlens") -> None:
     import torch
     if not isinstance(cu, torch.Tensor) or not cu.is_cuda or cu.dtype != torch.int32 or cu.numel() != desc.nseq + 1:
-        raise PvaError(PVA_ERR_INVALID_ARG, f"cu_seqlens must be a device int32 tensor of {desc.nseq + 1} entries")
+        raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a device int32 tensor of {desc.nseq + 1} entries")
+
+
+def _check_scales(desc: SegDesc, scales) -> None:
+    import torch
+    for name, s in scales:
+        if (not isinstance(s, torch.Tensor) or not s.is_cuda or s.dtype != torch.float32
+                or s.numel() != desc.nseq * desc.num_heads or not s.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be device float32 [{desc.nseq}, {desc.num_heads}]")
 
 
 def packed_attn_fwd(q, k, v, cu_seqlens, seg_desc: SegDesc, scale: float, out, stream=None):
@@ -228,14 +320,40 @@ def packed_attn_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, seg_desc
     """fp8 (E4M3FN codes + per-(sequence, head) fp32 scales) variant; bf16 ``out``."""
     import torch
     _check_qkvo(seg_desc, [("q", q), ("k", k), ("v", v)], (torch.float8_e4m3fn, torch.uint8), out)
-    for name, s in (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)):
-        if (not s.is_cuda or s.dtype != torch.float32 or s.numel() != seg_desc.nseq * seg_desc.num_heads
-                or not s.is_contiguous()):
-            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be device float32 [{seg_desc.nseq}, {seg_desc.num_heads}]")
+    _check_scales(seg_desc, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
     _check_cu(seg_desc, cu_seqlens)
     st = lib().packed_attn_fwd_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
                                    _ptr(cu_seqlens), seg_desc.handle, ctypes.c_float(scale), _ptr(out),
                                    ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
+
+
+def packed_attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDesc, scale: float, out, stream=None):
+    """bf16 forward where q / out hold only the queried rows ([total_q, H, D])
+    and k / v whole sequences; writes and returns ``out``."""
+    import torch
+    _check_qkvo(seg_desc, [("q", q), ("k", k), ("v", v)], (torch.bfloat16,), out)
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                      seg_desc.handle, ctypes.c_float(scale), _ptr(out),
+                                      ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
+
+
+def packed_attn_fwd_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDesc,
+                               scale: float, out, stream=None):
+    """fp8 (E4M3FN codes + per-(sequence, head) fp32 scales) variant of packed_attn_fwd_varlen."""
+    import torch
+    _check_qkvo(seg_desc, [("q", q), ("k", k), ("v", v)], (torch.float8_e4m3fn, torch.uint8), out)
+    _check_scales(seg_desc, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                          _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), seg_desc.handle,
+                                          ctypes.c_float(scale), _ptr(out), ctypes.c_void_p(_stream_handle(stream)))
     _check(st)
     return out
 

@@ -40,23 +40,29 @@ int hip_error(hipError_t e, const char* what) {
   return set_error(PVA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int check_cu(const int32_t* cu, const pva_seg_desc* d, hipStream_t stream) {
-  const char* env = std::getenv("PVA_CHECK");
-  if (!env || std::strcmp(env, "1") != 0) return PVA_OK;
-  std::vector<int32_t> host(d->plan.cu_seqlens.size());
+int check_one_cu(const int32_t* cu, const std::vector<int32_t>& want, const char* name, hipStream_t stream) {
+  std::vector<int32_t> host(want.size());
   hipError_t e = hipMemcpyAsync(host.data(), cu, host.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return hip_error(e, "PVA_CHECK: reading cu_seqlens");
-  if (host != d->plan.cu_seqlens)
-    return set_error(PVA_ERR_INVALID_ARG, "PVA_CHECK: device cu_seqlens differs from the descriptor's");
+  if (e != hipSuccess) return hip_error(e, (std::string("PVA_CHECK: reading ") + name).c_str());
+  if (host != want)
+    return set_error(PVA_ERR_INVALID_ARG, std::string("PVA_CHECK: device ") + name + " differs from the descriptor's");
   return PVA_OK;
 }
 
-int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                 float scale, void* out, pva_dtype want) {
+int check_cu(const int32_t* cu_q, const int32_t* cu_k, const pva_seg_desc* d, hipStream_t stream) {
+  const char* env = std::getenv("PVA_CHECK");
+  if (!env || std::strcmp(env, "1") != 0) return PVA_OK;
+  int st = check_one_cu(cu_k, d->plan.cu_seqlens, "cu_seqlens_k", stream);
+  if (st == PVA_OK && cu_q != cu_k) st = check_one_cu(cu_q, d->plan.cu_seqlens_q, "cu_seqlens_q", stream);
+  return st;
+}
+
+int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+                 const pva_seg_desc* d, float scale, void* out, pva_dtype want) {
   // every check here is host-only and runs before anything touches the device
   if (!d) return set_error(PVA_ERR_INVALID_ARG, "seg_desc is NULL");
-  if (!q || !k || !v || !out || !cu) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (!q || !k || !v || !out || !cu_q || !cu_k) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return set_error(PVA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (!(std::isfinite(scale) && scale > 0.0f)) return set_error(PVA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -66,8 +72,10 @@ int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu,
   return PVA_OK;
 }
 
-int build_common(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
-                 int32_t head_dim, pva_dtype dtype, bool upload, void* stream, pva_seg_desc** out) {
+// Builds a plan with `plan_fn` and, if asked, uploads the work list and the
+// key limits to the current device (one allocation: items, then limits).
+template <typename PlanFn>
+int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) {
   if (!out) return set_error(PVA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   pva_seg_desc* d = new (std::nothrow) pva_seg_desc();
@@ -75,7 +83,7 @@ int build_common(const int32_t* text_len, const int32_t* image_len, int32_t nseq
   std::string err;
   int st;
   try {
-    st = pva::build_plan(text_len, image_len, nseq, num_heads, head_dim, dtype, &d->plan, &err);
+    st = plan_fn(&d->plan, &err);
   } catch (const std::bad_alloc&) {
     st = PVA_ERR_NO_MEMORY;
     err = "host allocation failed";
@@ -92,29 +100,81 @@ int build_common(const int32_t* text_len, const int32_t* image_len, int32_t nseq
       return hip_error(e, "hipGetDevice");
     }
     d->device = dev;
-    const size_t bytes = d->plan.items.size() * sizeof(pva::WorkItem);
-    if (bytes > 0) {
-      e = hipMalloc(&d->d_items, bytes);
-      if (e != hipSuccess) {
-        d->d_items = nullptr;
-        delete d;
-        return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
-      }
-      e = hipMemcpyAsync(d->d_items, d->plan.items.data(), bytes, hipMemcpyHostToDevice,
-                         static_cast<hipStream_t>(stream));
-      if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
-      if (e != hipSuccess) {
-        (void)hipFree(d->d_items);
-        delete d;
-        return hip_error(e, "uploading the work list");
-      }
-    } else {
-      // every launch is empty; keep a non-null marker so the descriptor is launchable
-      d->d_items = reinterpret_cast<void*>(uintptr_t(1));
+    const size_t item_bytes = (d->plan.items.size() * sizeof(pva::WorkItem) + 255) / 256 * 256;
+    const size_t lim_bytes = d->plan.key_lim.size() * sizeof(int32_t);
+    void* base = nullptr;
+    e = hipMalloc(&base, item_bytes + lim_bytes);
+    if (e != hipSuccess) {
+      delete d;
+      return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
+    }
+    d->d_items = base;
+    d->d_lims = reinterpret_cast<int32_t*>(static_cast<char*>(base) + item_bytes);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (!d->plan.items.empty())
+      e = hipMemcpyAsync(d->d_items, d->plan.items.data(), d->plan.items.size() * sizeof(pva::WorkItem),
+                         hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(d->d_lims, d->plan.key_lim.data(), lim_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      (void)hipFree(base);
+      delete d;
+      return hip_error(e, "uploading the work list");
     }
   }
   *out = d;
   return ok();
+}
+
+int build_two(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads, int32_t head_dim,
+              pva_dtype dtype, bool upload, void* stream, pva_seg_desc** out) {
+  return build_common(
+      [&](pva::Plan* p, std::string* err) {
+        return pva::build_plan(text_len, image_len, nseq, num_heads, head_dim, dtype, p, err);
+      },
+      upload, stream, out);
+}
+
+int build_segs(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count, const int32_t* q_start,
+               int32_t nseq, int32_t num_heads, int32_t head_dim, pva_dtype dtype, bool upload, void* stream,
+               pva_seg_desc** out) {
+  return build_common(
+      [&](pva::Plan* p, std::string* err) {
+        return pva::build_plan_segments(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, p,
+                                        err);
+      },
+      upload, stream, out);
+}
+
+int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
+             const pva_seg_desc* d, float scale, void* out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_BF16);
+  if (st != PVA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
+  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, s);
+  if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
+  return ok();
+}
+
+int fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
+            const float* v_scale, const int32_t* cu_q, const int32_t* cu_k, const pva_seg_desc* d, float scale,
+            void* out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_FP8_E4M3);
+  if (st != PVA_OK) return st;
+  if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
+  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, s);
+  if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
+  if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
+  return ok();
+}
+
+int need_full_queries(const pva_seg_desc* d) {
+  if (d && d->plan.queries_suffix())
+    return set_error(PVA_ERR_INVALID_ARG, "seg_desc queries only a suffix of its sequences: use packed_attn_fwd_varlen");
+  return PVA_OK;
 }
 
 }  // namespace
@@ -123,18 +183,44 @@ extern "C" {
 
 int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                        int32_t head_dim, pva_dtype dtype, void* stream, pva_seg_desc** out) {
-  return build_common(text_len, image_len, nseq, num_heads, head_dim, dtype, true, stream, out);
+  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, true, stream, out);
 }
 
 int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                             int32_t head_dim, pva_dtype dtype, pva_seg_desc** out) {
-  return build_common(text_len, image_len, nseq, num_heads, head_dim, dtype, false, nullptr, out);
+  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, false, nullptr, out);
+}
+
+int pva_seg_desc_build_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                                pva_dtype dtype, void* stream, pva_seg_desc** out) {
+  return build_segs(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, true, stream, out);
+}
+
+int pva_seg_desc_build_segments_host(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                     const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                                     pva_dtype dtype, pva_seg_desc** out) {
+  return build_segs(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, false, nullptr, out);
 }
 
 int pva_seg_desc_cu_seqlens(const pva_seg_desc* d, const int32_t** host_cu, int32_t* len) {
   if (!d || !host_cu || !len) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
   *host_cu = d->plan.cu_seqlens.data();
   *len = static_cast<int32_t>(d->plan.cu_seqlens.size());
+  return ok();
+}
+
+int pva_seg_desc_cu_seqlens_q(const pva_seg_desc* d, const int32_t** host_cu_q, int32_t* len) {
+  if (!d || !host_cu_q || !len) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
+  *host_cu_q = d->plan.cu_seqlens_q.data();
+  *len = static_cast<int32_t>(d->plan.cu_seqlens_q.size());
+  return ok();
+}
+
+int pva_seg_desc_key_limits(const pva_seg_desc* d, const int32_t** key_limits, int32_t* len) {
+  if (!d || !key_limits || !len) return set_error(PVA_ERR_INVALID_ARG, "NULL argument");
+  *key_limits = d->plan.key_lim.data();
+  *len = static_cast<int32_t>(d->plan.key_lim.size());
   return ok();
 }
 
@@ -156,7 +242,7 @@ int pva_seg_desc_work_items(const pva_seg_desc* d, const int32_t** items, int32_
 
 void pva_seg_desc_free(pva_seg_desc* d) {
   if (!d) return;
-  if (d->d_items && d->d_items != reinterpret_cast<void*>(uintptr_t(1))) {
+  if (d->d_items) {
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != d->device && d->device >= 0) (void)hipSetDevice(d->device);
@@ -168,31 +254,34 @@ void pva_seg_desc_free(pva_seg_desc* d) {
 
 int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* cu_seqlens,
                     const pva_seg_desc* seg_desc, float scale, void* out, void* stream) {
-  int st = validate_fwd(q, k, v, cu_seqlens, seg_desc, scale, out, PVA_BF16);
+  int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = check_cu(cu_seqlens, seg_desc, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_bf16(q, k, v, cu_seqlens, seg_desc, scale, out, s);
-  if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
-  return ok();
+  return fwd_bf16(q, k, v, cu_seqlens, cu_seqlens, seg_desc, scale, out, stream);
+}
+
+int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                           const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
+                           void* stream) {
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, stream);
 }
 
 int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
                         const float* v_scale, const int32_t* cu_seqlens, const pva_seg_desc* seg_desc, float scale,
                         void* out, void* stream) {
-  int st = validate_fwd(q, k, v, cu_seqlens, seg_desc, scale, out, PVA_FP8_E4M3);
+  int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = check_cu(cu_seqlens, seg_desc, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, seg_desc, scale, out, s);
-  if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
-  if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
-  return ok();
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, cu_seqlens, seg_desc, scale, out, stream);
+}
+
+int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                               const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                               const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
+                               void* stream) {
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, stream);
 }
 
 const char* pva_last_error(void) { return g_last_error.c_str(); }
 
-const char* pva_version(void) { return "pva 0.1 gfx950"; }
+const char* pva_version(void) { return "pva 0.2 gfx950"; }
 
 }  // extern "C"

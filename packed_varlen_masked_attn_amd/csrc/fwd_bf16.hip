@@ -230,6 +230,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
                                                                     const __bf16* __restrict__ K,
                                                                     const __bf16* __restrict__ V,
                                                                     const int32_t* __restrict__ cu,
+                                                                    const int32_t* __restrict__ lims,
                                                                     const WorkItem* __restrict__ items, int H,
                                                                     float scale_log2, __bf16* __restrict__ O) {
   using Kn = Kernel<D>;
@@ -252,22 +253,27 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int T = it.text_len, L = it.seq_len;
+  const int L = it.seq_len;
   const int64_t rs = int64_t(H) * D;  // elements between consecutive tokens of one head
   const uint32_t rs2 = uint32_t(rs) * 2u;  // bytes (the planner keeps L * rs2 below 2^31)
   // bytes from a head's first row of the sequence to the end of its last row
   const uint32_t head_bytes = uint32_t(L - 1) * rs2 + 2u * D;
-  const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
-  const __bf16* Qh = Q + base;
+  const int32_t kseq = cu[it.seq];  // first K/V token of the sequence
+  const int64_t base = int64_t(kseq) * rs + int64_t(it.head) * D;
+  // Q and O hold the queried rows only: row r of the sequence is row qo_row + r - q0
+  const int64_t qbase = int64_t(it.qo_row - it.q0) * rs + int64_t(it.head) * D;
+  const __bf16* Qh = Q + qbase;
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + base);
 
-  // this lane's query row and its key limit; rows past the sequence end act
-  // as image rows (their outputs are never stored)
+  // this lane's query row and its key limit; rows past the sequence end see
+  // all L keys (their outputs are never stored). The limits never decrease
+  // along the rows, so the wave's first row has the smallest.
+  const int32_t* slim = lims + kseq;
   const int wrow0 = it.q0 + 32 * wave;
   const int qrow = wrow0 + l32;
-  const int mylim = key_limit(qrow, T, L);
-  const int wlim_min = key_limit(wrow0, T, L);  // smallest key limit of the wave's rows
+  const int mylim = qrow < L ? slim[qrow] : L;
+  const int wlim_min = wrow0 < L ? slim[wrow0] : L;
   const int kend = it.k_end;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
@@ -391,7 +397,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   const float lt = half_swap_sum(st.l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
   if (qrow < L) {
-    __bf16* orow = O + base + int64_t(qrow) * rs;
+    __bf16* orow = O + qbase + int64_t(qrow) * rs;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -412,7 +418,7 @@ int launch(const void* q, const void* k, const void* v, const int32_t* cu, const
   if (n == 0) return PVA_OK;
   const float scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
   hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, static_cast<const __bf16*>(q),
-                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu,
+                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu, d->d_lims,
                      static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2,
                      static_cast<__bf16*>(out));
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;

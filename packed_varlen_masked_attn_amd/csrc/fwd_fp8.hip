@@ -222,6 +222,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
                                                          const float* __restrict__ k_scale,
                                                          const float* __restrict__ v_scale,
                                                          const int32_t* __restrict__ cu,
+                                                         const int32_t* __restrict__ lims,
                                                          const WorkItem* __restrict__ items, int H,
                                                          float scale_log2e, __bf16* __restrict__ O) {
   using Kn = Fp8Kernel;
@@ -238,24 +239,31 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
-  const int T = it.text_len, L = it.seq_len;
+  const int L = it.seq_len;
   const int64_t rs = int64_t(H) * D;  // bytes (one byte per element) between tokens of one head
   const uint32_t rs32 = uint32_t(rs);  // the planner keeps L * rs below 2^31
   // bytes from a head's first row of the sequence to the end of its last row
   const uint32_t head_bytes = uint32_t(L - 1) * rs32 + uint32_t(D);
-  const int64_t base = int64_t(cu[it.seq]) * rs + int64_t(it.head) * D;
-  const uint8_t* Qh = Q + base;
+  const int32_t kseq = cu[it.seq];  // first K/V token of the sequence
+  const int64_t base = int64_t(kseq) * rs + int64_t(it.head) * D;
+  // Q and O hold the queried rows only: row r of the sequence is row qo_row + r - q0
+  const int64_t qbase = int64_t(it.qo_row - it.q0) * rs + int64_t(it.head) * D;
+  const uint8_t* Qh = Q + qbase;
   const uint8_t* Kb = K + base;
   const uint8_t* Vb = V + base;
   const int sh = it.seq * H + it.head;
   const float scale_log2 = q_scale[sh] * k_scale[sh] * scale_log2e;  // log2 units per raw score
   const float vs = v_scale[sh];
 
+  // this lane's query row and its key limit (rows past the end: L); the
+  // limits never decrease along the rows, so the wave's first row has the
+  // smallest
+  const int32_t* slim = lims + kseq;
   const int qrow = it.q0 + 32 * wave + l32;
-  const int mylim = key_limit(qrow, T, L);
+  const int mylim = qrow < L ? slim[qrow] : L;
   const int wrow0 = it.q0 + 32 * wave;
   const bool wave_active = wrow0 < L;
-  const int wlim_min = key_limit(wrow0, T, L);
+  const int wlim_min = wave_active ? slim[wrow0] : L;
   const int kend = it.k_end;
 
   typename Kn::KLoader kld;
@@ -383,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   if (wave_active && qrow < L) {
     const float lt = oacc[NDB][0];
     const float inv = lt > 0.0f ? vs / lt : 0.0f;
-    __bf16* orow = O + (int64_t(cu[it.seq]) + qrow) * H * D + int64_t(it.head) * D;
+    __bf16* orow = O + qbase + int64_t(qrow) * rs;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -406,7 +414,7 @@ int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs,
   if (n == 0) return PVA_OK;
   const float scale_log2e = static_cast<float>(double(scale) * 1.4426950408889634);
   hipLaunchKernelGGL(fwd_fp8_kernel, dim3(n), dim3(Fp8Cfg::NT), 0, stream, static_cast<const uint8_t*>(q),
-                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), qs, ks, vs, cu,
+                     static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), qs, ks, vs, cu, d->d_lims,
                      static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2e,
                      static_cast<__bf16*>(out));
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;

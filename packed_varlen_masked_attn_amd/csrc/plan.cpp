@@ -2,14 +2,21 @@
 //
 // The mask is the Generalized Causal Attention of "[RFC]: HunyuanImage 3.0
 // deployment" (Proposed Change P0, attention mask challenge; Model structure,
-// item 1): text rows causal over the text prefix, image rows see their whole
-// sequence. Its key limit lim(i) never decreases along i, so every row's
-// allowed keys are a prefix [0, lim(i)) and a query tile [qa, qb) needs:
+// item 1): a sequence is a list of segments; a token of a text (causal)
+// segment sees every key up to itself, a token of an image (full) block sees
+// every key up to the end of its block. Its key limit lim(i) never decreases
+// along i, so every row's allowed keys are a prefix [0, lim(i)) and a query
+// tile [qa, qb) needs:
 //   key tiles below floor(lim(qa) / BN)        : FULL (no mask at all)
 //   key tiles from ceil(lim(qb - 1) / BN) on    : SKIP (never loaded)
 //   key tiles in between                        : PARTIAL (element mask)
 // which is the block-sparse form the RFC names, and also its split into
-// causal and full segments, with no partial-result merge needed.
+// causal and full segments, with no partial-result merge needed. The
+// two-segment case (text prefix, one image block) is the RFC's packed batch.
+//
+// Queries may cover only a suffix [q_start, L) of a sequence (the prefix's
+// keys and values are reused; Model structure item 1, the single Prefix KV):
+// query tiles then start at q_start and Q / O hold only the queried rows.
 
 #include <algorithm>
 #include <cmath>
@@ -28,7 +35,7 @@ TileShape tile_shape(pva_dtype dtype, int32_t head_dim) {
 
 namespace {
 
-int fail(std::string* err, int code, const char* msg) {
+int fail(std::string* err, int code, const std::string& msg) {
   if (err) *err = msg;
   return code;
 }
@@ -39,68 +46,91 @@ struct Group {  // all query tiles of one (sequence, head)
   std::vector<WorkItem> items;
 };
 
-}  // namespace
+struct SeqSpec {
+  std::vector<int32_t> seg_len, seg_kind;
+  int32_t q_start = 0;
+};
 
-int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
-               int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err) {
-  if (!plan) return fail(err, PVA_ERR_INVALID_ARG, "plan output is NULL");
-  if (!text_len || !image_len) return fail(err, PVA_ERR_INVALID_ARG, "text_len/image_len is NULL");
+int check_shape(int32_t nseq, int32_t num_heads, int32_t head_dim, pva_dtype dtype, std::string* err) {
   if (nseq < 1) return fail(err, PVA_ERR_INVALID_ARG, "nseq must be >= 1");
   if (num_heads < 1) return fail(err, PVA_ERR_INVALID_ARG, "num_heads must be >= 1");
   if (dtype != PVA_BF16 && dtype != PVA_FP8_E4M3) return fail(err, PVA_ERR_INVALID_ARG, "unknown dtype");
   if (head_dim != 64 && head_dim != 128) return fail(err, PVA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (dtype == PVA_FP8_E4M3 && head_dim != 128)
     return fail(err, PVA_ERR_UNSUPPORTED, "the fp8 path supports head_dim 128 only");
+  return PVA_OK;
+}
 
+// Plans validated sequence specs (segment kinds and lengths checked by the callers).
+int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t head_dim, pva_dtype dtype,
+                   Plan* plan, std::string* err) {
+  const int32_t nseq = static_cast<int32_t>(seqs.size());
   Plan p;
   p.dtype = dtype;
   p.nseq = nseq;
   p.num_heads = num_heads;
   p.head_dim = head_dim;
   p.tile = tile_shape(dtype, head_dim);
-  p.text_len.assign(text_len, text_len + nseq);
-  p.image_len.assign(image_len, image_len + nseq);
   p.seq_len.resize(nseq);
-  p.cu_seqlens.resize(nseq + 1);
-  int64_t total = 0, pairs = 0;
-  p.cu_seqlens[0] = 0;
+  p.q_start.resize(nseq);
+  p.cu_seqlens.assign(nseq + 1, 0);
+  p.cu_seqlens_q.assign(nseq + 1, 0);
+  int64_t total = 0, total_q = 0, pairs = 0;
   for (int32_t s = 0; s < nseq; ++s) {
-    const int64_t T = text_len[s], I = image_len[s];
-    if (T < 0 || I < 0) return fail(err, PVA_ERR_INVALID_ARG, "text_len and image_len must be >= 0");
-    if (T + I < 1) return fail(err, PVA_ERR_INVALID_ARG, "every sequence needs at least one token");
-    if (T + I > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
+    int64_t L = 0;
+    for (int32_t n : seqs[s].seg_len) L += n;
+    if (L < 1) return fail(err, PVA_ERR_INVALID_ARG, "every sequence needs at least one token");
+    if (L > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
     // the kernels address one head's rows of a sequence with 32-bit byte
     // offsets below 2^31 (row stride H * D elements of at most 2 bytes)
-    if ((T + I) * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
+    if (L * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
       return fail(err, PVA_ERR_UNSUPPORTED, "sequence too long for 32-bit head addressing (L * H * D * 2 >= 2^31)");
-    total += T + I;
+    const int32_t qs = seqs[s].q_start;
+    if (qs < 0 || qs > L) return fail(err, PVA_ERR_INVALID_ARG, "q_start must lie in [0, L]");
+    total += L;
+    total_q += L - qs;
     if (total > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "packed token count exceeds int32");
-    p.seq_len[s] = static_cast<int32_t>(T + I);
+    p.seq_len[s] = static_cast<int32_t>(L);
+    p.q_start[s] = qs;
     p.cu_seqlens[s + 1] = static_cast<int32_t>(total);
-    pairs += T * (T + 1) / 2 + I * (T + I);
+    p.cu_seqlens_q[s + 1] = static_cast<int32_t>(total_q);
   }
   // element offsets are formed as (token * H + h) * D in int64 on the device
   if (total * int64_t(num_heads) * head_dim > (int64_t(1) << 62))
     return fail(err, PVA_ERR_INVALID_ARG, "tensor too large");
   p.total_tokens = total;
+  p.total_q = total_q;
+
+  // ---- key limits: lim(i) = i + 1 in a text segment, the block's end in an image block
+  p.key_lim.resize(static_cast<size_t>(total));
+  for (int32_t s = 0; s < nseq; ++s) {
+    int32_t* lim = p.key_lim.data() + p.cu_seqlens[s];
+    int32_t a = 0;
+    for (size_t g = 0; g < seqs[s].seg_len.size(); ++g) {
+      const int32_t b = a + seqs[s].seg_len[g];
+      for (int32_t i = a; i < b; ++i) lim[i] = seqs[s].seg_kind[g] == PVA_SEG_CAUSAL ? i + 1 : b;
+      a = b;
+    }
+    for (int32_t i = p.q_start[s]; i < p.seq_len[s]; ++i) pairs += lim[i];
+  }
   p.useful_flops = 4 * int64_t(head_dim) * num_heads * pairs;
 
   // ---- segment descriptors: per (sequence, query tile) tile classes
   const int32_t BM = p.tile.bm, BN = p.tile.bn;
   std::vector<std::vector<WorkItem>> seq_tiles(nseq);
   for (int32_t s = 0; s < nseq; ++s) {
-    const int32_t T = p.text_len[s], L = p.seq_len[s];
-    for (int32_t qa = 0; qa < L; qa += BM) {
+    const int32_t L = p.seq_len[s], qs = p.q_start[s];
+    const int32_t* lim = p.key_lim.data() + p.cu_seqlens[s];
+    for (int32_t qa = qs; qa < L; qa += BM) {
       const int32_t qb = std::min(qa + BM, L);
-      const int32_t lim_a = key_limit(qa, T, L), lim_b = key_limit(qb - 1, T, L);
       WorkItem w;
       w.seq = s;
       w.head = 0;
       w.q0 = qa;
       w.q_rows = qb - qa;
-      w.k_full_end = lim_a / BN;
-      w.k_end = (lim_b + BN - 1) / BN;
-      w.text_len = T;
+      w.k_full_end = lim[qa] / BN;
+      w.k_end = (lim[qb - 1] + BN - 1) / BN;
+      w.qo_row = p.cu_seqlens_q[s] + (qa - qs);
       w.seq_len = L;
       seq_tiles[s].push_back(w);
     }
@@ -112,6 +142,7 @@ int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, 
   std::vector<Group> groups;
   groups.reserve(size_t(nseq) * num_heads);
   for (int32_t s = 0; s < nseq; ++s) {
+    if (seq_tiles[s].empty()) continue;
     for (int32_t h = 0; h < num_heads; ++h) {
       Group g{s, h, 0, seq_tiles[s]};
       for (auto& w : g.items) {
@@ -149,6 +180,55 @@ int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, 
 
   *plan = std::move(p);
   return PVA_OK;
+}
+
+}  // namespace
+
+int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+               int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err) {
+  if (!plan) return fail(err, PVA_ERR_INVALID_ARG, "plan output is NULL");
+  if (!text_len || !image_len) return fail(err, PVA_ERR_INVALID_ARG, "text_len/image_len is NULL");
+  int st = check_shape(nseq, num_heads, head_dim, dtype, err);
+  if (st != PVA_OK) return st;
+  std::vector<SeqSpec> seqs(nseq);
+  for (int32_t s = 0; s < nseq; ++s) {
+    if (text_len[s] < 0 || image_len[s] < 0)
+      return fail(err, PVA_ERR_INVALID_ARG, "text_len and image_len must be >= 0");
+    if (int64_t(text_len[s]) + image_len[s] > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
+    seqs[s].seg_len = {text_len[s], image_len[s]};
+    seqs[s].seg_kind = {PVA_SEG_CAUSAL, PVA_SEG_FULL};
+  }
+  st = plan_sequences(seqs, num_heads, head_dim, dtype, plan, err);
+  if (st != PVA_OK) return st;
+  plan->text_len.assign(text_len, text_len + nseq);
+  plan->image_len.assign(image_len, image_len + nseq);
+  return PVA_OK;
+}
+
+int build_plan_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                        const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                        pva_dtype dtype, Plan* plan, std::string* err) {
+  if (!plan) return fail(err, PVA_ERR_INVALID_ARG, "plan output is NULL");
+  if (!seg_len || !seg_kind || !seg_count) return fail(err, PVA_ERR_INVALID_ARG, "a segment array is NULL");
+  int st = check_shape(nseq, num_heads, head_dim, dtype, err);
+  if (st != PVA_OK) return st;
+  std::vector<SeqSpec> seqs(nseq);
+  int64_t g = 0;
+  for (int32_t s = 0; s < nseq; ++s) {
+    if (seg_count[s] < 1) return fail(err, PVA_ERR_INVALID_ARG, "every sequence needs at least one segment");
+    int64_t L = 0;
+    for (int32_t k = 0; k < seg_count[s]; ++k, ++g) {
+      if (seg_len[g] < 0) return fail(err, PVA_ERR_INVALID_ARG, "segment lengths must be >= 0");
+      if (seg_kind[g] != PVA_SEG_CAUSAL && seg_kind[g] != PVA_SEG_FULL)
+        return fail(err, PVA_ERR_INVALID_ARG, "segment kind must be PVA_SEG_CAUSAL or PVA_SEG_FULL");
+      L += seg_len[g];
+      if (L > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
+      seqs[s].seg_len.push_back(seg_len[g]);
+      seqs[s].seg_kind.push_back(seg_kind[g]);
+    }
+    seqs[s].q_start = q_start ? q_start[s] : 0;
+  }
+  return plan_sequences(seqs, num_heads, head_dim, dtype, plan, err);
 }
 
 }  // namespace pva

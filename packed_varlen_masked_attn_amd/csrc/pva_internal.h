@@ -25,7 +25,7 @@ struct WorkItem {
   int32_t q_rows;  // valid rows in the tile (<= BM)
   int32_t k_full_end;
   int32_t k_end;
-  int32_t text_len;
+  int32_t qo_row;  // row of Q and O holding query row q0 (packed queried rows)
   int32_t seq_len;
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
@@ -55,26 +55,33 @@ struct Plan {
   pva_dtype dtype = PVA_BF16;
   int32_t nseq = 0, num_heads = 0, head_dim = 0;
   TileShape tile{0, 0};
-  std::vector<int32_t> text_len, image_len, seq_len, cu_seqlens;
-  std::vector<WorkItem> items;  // launch order, XCD-interleaved, padded with empty slots
+  std::vector<int32_t> text_len, image_len;  // two-segment builds only (for inspection)
+  std::vector<int32_t> seq_len, q_start;     // per sequence
+  std::vector<int32_t> cu_seqlens;           // K/V token offsets [nseq + 1]
+  std::vector<int32_t> cu_seqlens_q;         // Q/O row offsets [nseq + 1] (equal when q_start == 0)
+  std::vector<int32_t> key_lim;              // per K/V token: allowed keys of that row are [0, lim)
+  std::vector<WorkItem> items;               // launch order, XCD-interleaved, padded with empty slots
   int64_t useful_flops = 0;
   int64_t total_tokens = 0;
+  int64_t total_q = 0;
+  bool queries_suffix() const { return total_q != total_tokens; }
 };
 
-// Mask key limit of row i of a sequence: keys [0, lim) are allowed.
-PVA_HOST_DEVICE inline int32_t key_limit(int32_t i, int32_t text_len, int32_t seq_len) {
-  return i < text_len ? i + 1 : seq_len;
-}
-
 // Validates and plans; on failure returns a status and fills `err`.
+// Two segments per sequence: text (causal) then one image block (full).
 int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err);
+// Any number of segments per sequence and an optional first queried row.
+int build_plan_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                        const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
+                        pva_dtype dtype, Plan* plan, std::string* err);
 
 }  // namespace pva
 
 // The descriptor handed across the C-ABI.
 struct pva_seg_desc {
   pva::Plan plan;
-  void* d_items = nullptr;  // device copy of plan.items (nullptr for host-only descriptors)
-  int32_t device = -1;      // HIP device the work list lives on
+  void* d_items = nullptr;    // device copy of plan.items (nullptr for host-only descriptors)
+  int32_t* d_lims = nullptr;  // device copy of plan.key_lim (same allocation as d_items)
+  int32_t device = -1;        // HIP device the work list lives on
 };

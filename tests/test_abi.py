@@ -151,3 +151,43 @@ def test_accessor_null_args():
     assert L.pva_seg_desc_cu_seqlens(None, None, None) == pva.PVA_ERR_INVALID_ARG
     assert L.pva_seg_desc_work_items(None, None, None) == pva.PVA_ERR_INVALID_ARG
     L.pva_seg_desc_free(None)  # no-op
+
+
+def test_suffix_descriptor_needs_the_varlen_entry_points():
+    L = pva.lib()
+    desc = pva.SegDesc.segments([([16, 48], [pva.SEG_CAUSAL, pva.SEG_FULL], 16)], 2, 64, host_only=True)
+    p = ctypes.c_void_p(FAKE)
+    st = L.packed_attn_fwd(p, p, p, p, desc.handle, ctypes.c_float(0.1), p, None)
+    assert st == pva.PVA_ERR_INVALID_ARG and "varlen" in L.pva_last_error().decode()
+    # the varlen entry point gets past that check and stops at the host-only one
+    st = L.packed_attn_fwd_varlen(p, p, p, p, p, desc.handle, ctypes.c_float(0.1), p, None)
+    assert st == pva.PVA_ERR_INVALID_ARG and "host-only" in L.pva_last_error().decode()
+    d8 = pva.SegDesc.segments([([16, 48], [pva.SEG_CAUSAL, pva.SEG_FULL], 16)], 2, 128, "fp8", host_only=True)
+    st = L.packed_attn_fwd_fp8(p, p, p, p, p, p, p, d8.handle, ctypes.c_float(0.1), p, None)
+    assert st == pva.PVA_ERR_INVALID_ARG and "varlen" in L.pva_last_error().decode()
+
+
+@pytest.mark.parametrize("which", ["null_cu_q", "null_cu_k", "null_out", "wrong_dtype"])
+def test_varlen_rejects_on_host(which):
+    L = pva.lib()
+    desc = pva.SegDesc.segments([([4, 4], [0, 1], 2)], 2, 64, host_only=True)
+    p = ctypes.c_void_p(FAKE)
+    cq = ck = out = p
+    if which == "null_cu_q":
+        cq = None
+    elif which == "null_cu_k":
+        ck = None
+    elif which == "null_out":
+        out = None
+    if which == "wrong_dtype":
+        st = L.packed_attn_fwd_varlen_fp8(p, p, p, p, p, p, cq, ck, desc.handle, ctypes.c_float(0.1), out, None)
+    else:
+        st = L.packed_attn_fwd_varlen(p, p, p, cq, ck, desc.handle, ctypes.c_float(0.1), out, None)
+    assert st == pva.PVA_ERR_INVALID_ARG
+
+
+def test_new_accessor_null_args():
+    L = pva.lib()
+    assert L.pva_seg_desc_cu_seqlens_q(None, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_seg_desc_key_limits(None, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_seg_desc_build_segments_host(None, None, None, None, 1, 1, 64, 0, None) == pva.PVA_ERR_INVALID_ARG

@@ -50,11 +50,14 @@ def _check_plan(t, i, H, D, dtype="bf16"):
     real = items[items[:, 0] >= 0]
     # exact coverage: every (seq, head, q-tile) exactly once
     seen = {}
-    for seq, head, q0, q_rows, kfe, ke, T, L in real.tolist():
+    cu = desc.cu_seqlens
+    assert desc.cu_seqlens_q.tolist() == cu.tolist()  # every row is queried
+    for seq, head, q0, q_rows, kfe, ke, qo_row, L in real.tolist():
         key = (seq, head, q0)
         assert key not in seen
-        seen[key] = (q_rows, kfe, ke, T, L)
-        assert T == t[seq] and L == seq_len[seq]
+        seen[key] = (q_rows, kfe, ke, qo_row, L)
+        T = t[seq]
+        assert L == seq_len[seq] and qo_row == cu[seq] + q0
         assert q0 % BM == 0 and q_rows == min(BM, L - q0) and q_rows >= 1
         assert 0 <= kfe <= ke <= (L + BN - 1) // BN
         assert _desc_classes(kfe, ke, L, BN) == _classes_from_mask(T, L, q0, q_rows, BN)
@@ -126,3 +129,105 @@ def test_tile_visit_counts_mixed_res():
             p2 += sum(c == "P" for c in cls)
     assert (visits, partial) == (v2, p2)
     assert visits < dense
+
+
+# ---- general descriptors: several segments per sequence, queried suffixes
+def _check_plan_segments(seqs, H, D, dtype="bf16"):
+    desc = pva.SegDesc.segments(seqs, H, D, dtype=dtype, host_only=True)
+    BM, BN = desc.tile
+    Ls = [s.length for s in seqs]
+    assert desc.cu_seqlens.tolist() == oracle.offsets(Ls).tolist()
+    assert desc.cu_seqlens_q.tolist() == oracle.offsets([s.q_rows for s in seqs]).tolist()
+    assert desc.useful_flops == oracle.segment_useful_flops(seqs, H, D)
+    lims = desc.key_limits
+    cu, cuq = desc.cu_seqlens, desc.cu_seqlens_q
+    masks = [oracle.segment_mask(s.seg_len, s.seg_kind) for s in seqs]
+    for si, m in enumerate(masks):
+        assert lims[cu[si]:cu[si + 1]].tolist() == m.sum(axis=1).tolist()
+    items = desc.work_items
+    real = items[items[:, 0] >= 0]
+    seen = set()
+    for seq, head, q0, q_rows, kfe, ke, qo_row, L in real.tolist():
+        s = seqs[seq]
+        assert (seq, head, q0) not in seen
+        seen.add((seq, head, q0))
+        assert L == s.length and q0 >= s.q_start and (q0 - s.q_start) % BM == 0
+        assert q_rows == min(BM, L - q0) and qo_row == cuq[seq] + q0 - s.q_start
+        m = masks[seq][q0:q0 + q_rows]
+        n_kt = (L + BN - 1) // BN
+        cls = []
+        for kt in range(n_kt):
+            blk = m[:, kt * BN:(kt + 1) * BN]
+            cls.append("F" if (blk.all() and blk.shape[1] == BN) else ("P" if blk.any() else "S"))
+        assert _desc_classes(kfe, ke, L, BN) == tuple(cls)
+    want = {(si, h, q0) for si, s in enumerate(seqs) for h in range(H) for q0 in range(s.q_start, s.length, BM)}
+    assert seen == want
+    desc.close()
+
+
+def _random_segment_seqs(rng, nseq, max_segs=6, max_len=300, suffix=True):
+    seqs = []
+    for _ in range(nseq):
+        n = int(rng.integers(1, max_segs + 1))
+        lens = [int(x) for x in rng.integers(0, max_len + 1, n)]
+        if sum(lens) == 0:
+            lens[-1] = 1
+        kinds = [int(x) for x in rng.integers(0, 2, n)]
+        L = sum(lens)
+        qs = int(rng.integers(0, L + 1)) if suffix and rng.random() < 0.7 else 0
+        seqs.append(oracle.make_seq(lens, kinds, qs))
+    return seqs
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_plan_segments_random(seed):
+    rng = np.random.default_rng(900 + seed)
+    seqs = _random_segment_seqs(rng, int(rng.integers(1, 5)))
+    dtype = "fp8" if seed % 4 == 3 else "bf16"
+    D = 128 if dtype == "fp8" else int(rng.choice([64, 128]))
+    _check_plan_segments(seqs, int(rng.integers(1, 4)), D, dtype)
+
+
+def test_plan_two_segment_equivalence():
+    # the segment builder with {CAUSAL T, FULL I} plans exactly like the two-segment builder
+    w = workloads.mixed_res()
+    a = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, host_only=True)
+    b = pva.SegDesc.segments([([t, i], [pva.SEG_CAUSAL, pva.SEG_FULL]) for t, i in zip(w.text_len, w.image_len)],
+                             w.num_heads, w.head_dim, host_only=True)
+    assert np.array_equal(a.work_items, b.work_items)
+    assert np.array_equal(a.key_limits, b.key_limits)
+    assert a.useful_flops == b.useful_flops
+
+
+def test_plan_prefix_queries_mixed_res():
+    # image rows only (the prefix's K/V reused): useful work drops by the text rows' share
+    w = workloads.mixed_res()
+    seqs = [oracle.make_seq([t, i], [oracle.CAUSAL, oracle.FULL], t) for t, i in zip(w.text_len, w.image_len)]
+    _check_plan_segments(seqs, 4, 128)
+    d = pva.SegDesc.segments(seqs, w.num_heads, w.head_dim, host_only=True)
+    assert d.total_q == sum(w.image_len)
+    full = oracle.useful_flops(w.text_len, w.image_len, w.num_heads, w.head_dim)
+    text = 4 * 128 * 32 * sum(t * (t + 1) // 2 for t in w.text_len)
+    assert d.useful_flops == full - text
+
+
+@pytest.mark.parametrize("seqs,code", [
+    ([([1, 2], [0, 1, 0])], pva.PVA_ERR_INVALID_ARG),   # kinds count differs (caught by the binding)
+    ([([1, -2], [0, 1])], pva.PVA_ERR_INVALID_ARG),     # negative length
+    ([([1, 2], [0, 2])], pva.PVA_ERR_INVALID_ARG),      # unknown kind
+    ([([0, 0], [0, 1])], pva.PVA_ERR_INVALID_ARG),      # no token
+    ([([3, 2], [0, 1], 6)], pva.PVA_ERR_INVALID_ARG),   # q_start > L
+    ([([3, 2], [0, 1], -1)], pva.PVA_ERR_INVALID_ARG),  # q_start < 0
+    ([([], [])], pva.PVA_ERR_INVALID_ARG),               # no segment
+])
+def test_segments_rejected(seqs, code):
+    with pytest.raises(pva.PvaError) as e:
+        pva.SegDesc.segments(seqs, 2, 64, host_only=True)
+    assert e.value.status == code
+
+
+def test_segments_q_start_at_end_has_no_items():
+    d = pva.SegDesc.segments([([5, 3], [0, 1], 8), ([2], [1])], 2, 64, host_only=True)
+    items = d.work_items
+    assert set(items[items[:, 0] >= 0][:, 0].tolist()) == {1}
+    assert d.cu_seqlens_q.tolist() == [0, 0, 2]

@@ -3,7 +3,8 @@
 This module is shared by the test-side oracle and the HIP path. It holds
 shapes and random draws only: no part of the attention arithmetic, no mask,
 no offsets into the packed token axis. Each side derives those itself from
-the per-sequence (text_len, image_len) lists returned here.
+the per-sequence (text_len, image_len) lists, or the segment lists, returned
+here.
 
 Workload recipe (the pages publish no tensors, so every input is synthetic):
 
@@ -105,12 +106,108 @@ def mixed_res_fp8() -> Workload:
     return mixed_res("fp8")
 
 
+# ---------------------------------------------------------------------------
+# Multi-segment contexts and queried suffixes ("[RFC]: HunyuanImage 3.0
+# deployment", Model structure item 1: contexts interleave text and image
+# segments under Generalized Causal Attention, and one Prefix KV is computed
+# once and reused). Segment kinds: 0 = text (causal), 1 = image block (full).
+
+@dataclasses.dataclass(frozen=True)
+class SegWorkload:
+    """Packed sequences given as segment lists, each with its first queried row."""
+
+    name: str
+    seqs: Tuple[Tuple[Tuple[int, ...], Tuple[int, ...], int], ...]  # (seg_len, seg_kind, q_start)
+    num_heads: int
+    head_dim: int
+    seed: int
+    dtype: str  # "bf16" or "fp8"
+    description: str = ""
+
+    @property
+    def nseq(self) -> int:
+        return len(self.seqs)
+
+    @property
+    def seq_len(self) -> Tuple[int, ...]:
+        return tuple(int(sum(s[0])) for s in self.seqs)
+
+    @property
+    def q_rows(self) -> Tuple[int, ...]:
+        return tuple(int(sum(s[0])) - int(s[2]) for s in self.seqs)
+
+    @property
+    def total_tokens(self) -> int:
+        return int(sum(self.seq_len))
+
+    @property
+    def total_q(self) -> int:
+        return int(sum(self.q_rows))
+
+
+def seg_draw_f32(w: SegWorkload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Q [total_q, H, D] and K, V [total_tokens, H, D] as float32: Q, K and V
+    are drawn for every token in q, k, v order from default_rng(seed); Q then
+    keeps only the queried rows (so a suffix-queried workload shares its
+    query values with the fully queried one of the same seed)."""
+    rng = np.random.default_rng(w.seed)
+    shape = (w.total_tokens, w.num_heads, w.head_dim)
+    q = rng.standard_normal(shape, dtype=np.float32)
+    k = rng.standard_normal(shape, dtype=np.float32)
+    v = rng.standard_normal(shape, dtype=np.float32)
+    keep, a = [], 0
+    for L, (_, _, qs) in zip(w.seq_len, w.seqs):
+        keep.append(np.arange(a + int(qs), a + L))
+        a += L
+    return q[np.concatenate(keep).astype(np.int64)], k, v
+
+
+def seg_bf16_inputs(w: SegWorkload):
+    q, k, v = seg_draw_f32(w)
+    return to_bf16(q), to_bf16(k), to_bf16(v)
+
+
+def seg_fp8_inputs(w: SegWorkload):
+    """(q8, k8, v8, q_scale, k_scale, v_scale); Q's scales cover its queried rows."""
+    q, k, v = seg_draw_f32(w)
+    q8, qs = quantize_e4m3_rows(q, w.q_rows)
+    k8, ks = quantize_e4m3_rows(k, w.seq_len)
+    v8, vs = quantize_e4m3_rows(v, w.seq_len)
+    return q8, k8, v8, qs, ks, vs
+
+
+def mixed_res_prefix(dtype: str = "bf16") -> SegWorkload:
+    """The mixed-resolution batch with only its image rows queried: the text
+    prefix's K/V are computed once and reused, as in a denoising step."""
+    base = mixed_res()
+    seqs = tuple(((t, i), (0, 1), t) for t, i in zip(base.text_len, base.image_len))
+    return SegWorkload("mixed_res_prefix_kv" + ("_fp8" if dtype == "fp8" else ""), seqs, 32, 128, 2, dtype,
+                       "mixed-resolution CFG batch, image rows queried against text prefix + image K/V")
+
+
+def edit_segments(dtype: str = "bf16") -> SegWorkload:
+    """Four requests (CFG pairs) of interleaved segments: text prompt, a
+    1024-token conditioning image block, a 32-token text instruction, then
+    the generated image block (1024, 2304, 4096 and 3840 tokens)."""
+    prompts = mixed_res_text_lengths(0, 4)
+    seqs = []
+    for t1, img in zip(prompts, (1024, 2304, 4096, 3840)):
+        seq = ((t1, 1024, 32, img), (0, 1, 0, 1), 0)
+        seqs += [seq, seq]
+    return SegWorkload("edit_segments" + ("_fp8" if dtype == "fp8" else ""), tuple(seqs), 32, 128, 4, dtype,
+                       "text / conditioning image / text / generated image, four CFG pairs, all rows queried")
+
+
 WORKLOADS = {
     "tiny": tiny,
     "single_1024": single_1024,
     "mixed_res": mixed_res,
     "sp4_share": sp4_share_4096,
     "mixed_res_fp8": mixed_res_fp8,
+    "mixed_res_prefix": mixed_res_prefix,
+    "mixed_res_prefix_fp8": lambda: mixed_res_prefix("fp8"),
+    "edit_segments": edit_segments,
+    "edit_segments_fp8": lambda: edit_segments("fp8"),
 }
 
 
@@ -151,24 +248,34 @@ def seq_bounds(w: Workload) -> List[Tuple[int, int]]:
     return out
 
 
-def quantize_e4m3(x: np.ndarray, w: Workload):
-    """Per-(sequence, head) absmax quantisation of one float32 [N, H, D] tensor.
+def quantize_e4m3_rows(x: np.ndarray, rows: Sequence[int]):
+    """Per-(sequence, head) absmax quantisation of one float32 [N, H, D] tensor
+    whose sequences hold ``rows[s]`` consecutive rows each.
 
     Returns (codes, scales): codes is a CPU torch float8_e4m3fn tensor [N, H, D];
-    scales is float32 [nseq, H]. A (sequence, head) slice that is all zero gets
-    scale 1 so that its codes are zero.
+    scales is float32 [nseq, H]. A (sequence, head) slice that is all zero (or
+    empty) gets scale 1 so that its codes are zero.
     """
     import torch
+    H = x.shape[1]
     codes = np.empty(x.shape, dtype=np.float32)
-    scales = np.empty((w.nseq, w.num_heads), dtype=np.float32)
-    for s, (a, b) in enumerate(seq_bounds(w)):
-        blk = x[a:b]  # [L, H, D]
-        amax = np.abs(blk).max(axis=(0, 2)).astype(np.float32) if b > a else np.zeros(w.num_heads, np.float32)
+    scales = np.empty((len(rows), H), dtype=np.float32)
+    a = 0
+    for s, n in enumerate(rows):
+        b = a + int(n)
+        blk = x[a:b]  # [rows, H, D]
+        amax = np.abs(blk).max(axis=(0, 2)).astype(np.float32) if b > a else np.zeros(H, np.float32)
         sc = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
         scales[s] = sc
         codes[a:b] = np.clip(blk / sc[None, :, None], -E4M3_MAX, E4M3_MAX)
+        a = b
     t = torch.from_numpy(codes).to(torch.float8_e4m3fn)
     return t, scales
+
+
+def quantize_e4m3(x: np.ndarray, w: Workload):
+    """Per-(sequence, head) absmax quantisation of one float32 [N, H, D] tensor of workload ``w``."""
+    return quantize_e4m3_rows(x, w.seq_len)
 
 
 def fp8_inputs(w: Workload):
