@@ -50,19 +50,29 @@ struct Bf16Cfg {
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
   static constexpr int NS = 4;             // LDS stages per tensor
-  // K rows are padded by one 16-byte chunk: the 16 consecutive rows a K
-  // operand read touches at one chunk then fall on 16 different bank groups,
-  // and the address stays affine in the chunk (one base register).
-  static constexpr int KROW = C + 1;                        // chunks per padded K row
-  // 16-byte slots of a K / V stage, rounded up to whole 64-lane DMA rounds
-  static constexpr int KSLOTS = (BN * KROW + 63) / 64 * 64;
+  // K and V tiles are stored unpadded (C 16-byte chunks per row), with the
+  // chunks of each row XOR-permuted so that the MFMA operand reads are free of
+  // LDS bank conflicts:
+  //  * K is read 16 bytes per lane, 16 consecutive rows per LDS cycle at one
+  //    logical chunk: swz_k spreads those 16 reads over 16 bank groups;
+  //  * V is read with ds_read_b64_tr_b16, 4 consecutive rows x 64 bytes per
+  //    half-wave: swz_v (whole 64-byte quarters) puts the 4 rows in 4
+  //    different quarters of the 256-byte bank window.
+  // Both depend on the row only through bits that the per-step row offsets
+  // (16 kc, +8) keep, so each lane needs one address per K chunk and one per
+  // 32-column V block, and the step offsets are immediates.
+  static constexpr int KSLOTS = BN * C;
   static constexpr int KTILE = KSLOTS * 16;
-  // V rows are padded by 64 bytes: the four consecutive rows a transpose read
-  // touches then sit in four different 64-byte quarters of the bank window,
-  // and the address stays affine in the column block (one base register).
-  static constexpr int VROW = C + 4;                        // chunks per padded V row
-  static constexpr int VSLOTS = (BN * VROW + 63) / 64 * 64;
+  static constexpr int VSLOTS = BN * C;
   static constexpr int VTILE = VSLOTS * 16;
+  static __device__ __forceinline__ int swz_k(int r) { return ((r * C) / 16) % C; }
+  static __device__ __forceinline__ int swz_v(int r) { return 4 * (((r * C) / 16) % (C / 4)); }
+  struct KMap {
+    static __device__ __forceinline__ int chunk(int r, int pos) { return pos ^ swz_k(r); }
+  };
+  struct VMap {
+    static __device__ __forceinline__ int chunk(int r, int pos) { return pos ^ swz_v(r); }
+  };
   // DMA instructions every wave issues per tile (some waves issue one more);
   // the partial vmcnt waits count only these, so waves with more loads in
   // flight simply wait a little longer
@@ -81,32 +91,45 @@ struct Kernel {
   typedef short s16x8 __attribute__((ext_vector_type(8)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-  // ---- K and V tiles: rows padded to KROW / VROW 16-byte slots
-  using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
-  using VLoader = BufLoader<Cfg::NT, Cfg::VROW, Cfg::VSLOTS, PaddedRows<C>>;
+  // ---- K and V tiles: unpadded rows, XOR-permuted chunks
+  using KLoader = BufLoader<Cfg::NT, C, Cfg::KSLOTS, typename Cfg::KMap>;
+  using VLoader = BufLoader<Cfg::NT, C, Cfg::VSLOTS, typename Cfg::VMap>;
 
-  // ---- K operand of d-chunk c: row l32, chunk 2c + g of the padded tile
-  static __device__ __forceinline__ bf16x8 read_k(const uint8_t* kst, int c, int l32, int g) {
-    return *reinterpret_cast<const bf16x8*>(kst + 16 * (l32 * Cfg::KROW + 2 * c + g));
+  // Per-lane byte offsets (within a stage) of the operand reads: K chunk c of
+  // row l32; V^T block db of rows v_row0 (steps add 16 kc rows, +8 rows).
+  struct ReadAddr {
+    uint32_t k[NKC];
+    uint32_t v[NDB];
+    __device__ __forceinline__ void init(int l32, int g, int v_row0, int v_col) {
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) k[c] = uint32_t(16 * (C * l32 + ((2 * c + g) ^ Cfg::swz_k(l32))));
+      const int hv = Cfg::swz_v(v_row0) / 4;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) v[db] = uint32_t(16 * C * v_row0 + 64 * (db ^ hv) + 2 * v_col);
+    }
+  };
+
+  // ---- K operand of d-chunk c
+  static __device__ __forceinline__ bf16x8 read_k(const uint8_t* kst, int c, const ReadAddr& ra) {
+    return *reinterpret_cast<const bf16x8*>(kst + ra.k[c]);
   }
 
-  // ---- V^T operand of PV step `step` (16-key step kc, 32-column block db):
-  // rows 16 kc + v_row0 (+8), columns 32 db + v_col .. +3 of the padded tile
-  static __device__ __forceinline__ s16x8 read_v_step(const uint8_t* vst, int step, int v_row0, int v_col) {
+  // ---- V^T operand of PV step `step` (16-key step kc, 32-column block db)
+  static __device__ __forceinline__ s16x8 read_v_step(const uint8_t* vst, int step, const ReadAddr& ra) {
     const int kc = step / NDB, db = step % NDB;
-    const uint8_t* p0 = vst + 16 * Cfg::VROW * (16 * kc + v_row0) + 2 * (32 * db + v_col);
-    const uint8_t* p1 = p0 + 16 * Cfg::VROW * 8;
+    const uint8_t* p0 = vst + ra.v[db] + 16 * C * 16 * kc;
+    const uint8_t* p1 = p0 + 16 * C * 8;
     const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p0));
     const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((PVA_LDS s16x4*)(p1));
     return s16x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
   // ---- S^T = K Q^T of one tile (prologue only; the loop interleaves it)
-  static __device__ __forceinline__ f32x16 s_tile(const uint8_t* kst, const bf16x8 (&qf)[NKC], int l32, int g) {
+  static __device__ __forceinline__ f32x16 s_tile(const uint8_t* kst, const bf16x8 (&qf)[NKC], const ReadAddr& ra) {
     f32x16 s = {};
 #pragma unroll
     for (int c = 0; c < NKC; ++c)
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(kst, c, l32, g), qf[c], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_k(kst, c, ra), qf[c], s, 0, 0, 0);
     return s;
   }
 
@@ -127,17 +150,17 @@ struct Kernel {
   static constexpr int NSTEP = 2 * NDB;
   static __device__ __forceinline__ void s_phase(f32x16& snext, const uint8_t* kst, const bf16x8 (&qf)[NKC],
                                                  const f32x16& scur, float scale_log2, float m, float (&e)[16],
-                                                 uint32_t (&pk)[8], int l32, int g, s16x8 (&va)[NSTEP],
-                                                 const uint8_t* vst, int v_row0, int v_col) {
+                                                 uint32_t (&pk)[8], const ReadAddr& ra, s16x8 (&va)[NSTEP],
+                                                 const uint8_t* vst) {
     bf16x8 ka[3];
-    ka[0] = read_k(kst, 0, l32, g);
-    if (NKC > 1) ka[1] = read_k(kst, 1, l32, g);
+    ka[0] = read_k(kst, 0, ra);
+    if (NKC > 1) ka[1] = read_k(kst, 1, ra);
 #pragma unroll
-    for (int step = 0; step < NSTEP / 2; ++step) va[step] = read_v_step(vst, step, v_row0, v_col);
+    for (int step = 0; step < NSTEP / 2; ++step) va[step] = read_v_step(vst, step, ra);
     snext = f32x16{};
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
-      if (c + 2 < NKC) ka[(c + 2) % 3] = read_k(kst, c + 2, l32, g);
+      if (c + 2 < NKC) ka[(c + 2) % 3] = read_k(kst, c + 2, ra);
       snext = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[c % 3], qf[c], snext, 0, 0, 0);
 #pragma unroll
       for (int i = c * EPC; i < (c + 1) * EPC; ++i) e[i] = fast_exp2(fmaf(scur[i], scale_log2, -m));
@@ -147,7 +170,7 @@ struct Kernel {
       }
       if (c == (NKC > 1 ? 1 : 0)) {
 #pragma unroll
-        for (int step = NSTEP / 2; step < NSTEP; ++step) va[step] = read_v_step(vst, step, v_row0, v_col);
+        for (int step = NSTEP / 2; step < NSTEP; ++step) va[step] = read_v_step(vst, step, ra);
       }
       }
     // consume the results in an empty asm: the compiler must compute them
@@ -280,17 +303,15 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   // (tile t's resource starts at key row t * BN and ends with the sequence)
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;
-  // V's extra DMA rounds go to the waves that issue none for K
-  const int vwave = (wave + Cfg::NW / 2) % Cfg::NW;
   kld.init(rs2, lane, wave);
-  vld.init(rs2, lane, vwave);
+  vld.init(rs2, lane, wave);
   auto ld_k = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs2;
     kld.load(make_rsrc(Kb + o, head_bytes - o), stage, wave);
   };
   auto ld_v = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs2;
-    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, vwave);
+    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, wave);
   };
   if (kend > 0) ld_k(0, kst[0]);
   if (kend > 1) ld_k(1, kst[1]);
@@ -315,9 +336,9 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
   RowState st{-INFINITY, 0.0f};
 
-  // per-lane constant parts of the V^T (transpose-read) addresses
-  const int v_row0 = 4 * g + (lane & 15) / 4;
-  const int v_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // per-lane LDS offsets of the K and V^T (transpose-read) operands
+  typename Kn::ReadAddr ra;
+  ra.init(l32, g, 4 * g + (lane & 15) / 4, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   // K0, K1, V0 must have landed; K2 V1 K3 V2 may still be in flight
   if (kend > 3)
@@ -331,7 +352,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   // row's key limit, are computed masked: their probabilities are exactly
   // zero. That keeps every branch in the loop scalar and rare.
   if (kend > 0) {
-    sa = Kn::s_tile(kst[0], qf, l32, g);
+    sa = Kn::s_tile(kst[0], qf, ra);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
     st.m = Kn::tile_max(sa, scale_log2);  // first tile: O and l are still zero
   }
@@ -349,8 +370,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
     s16x8 va[Kn::NSTEP];  // V^T operands of PV(j), read during phase 1
     float e[16];
     uint32_t pk[8];
-    Kn::s_phase(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st.m, e, pk, l32, g, va, vst[SJ], v_row0,
-                v_col);
+    Kn::s_phase(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st.m, e, pk, ra, va, vst[SJ]);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     float mx, psum;
     Kn::pv_phase(oacc, va, e, pk, snext, mx, psum);
