@@ -20,7 +20,10 @@ Pins (all in tests/test_oracle.py, run without a GPU):
   * multi-segment masks (``oracle.segments``): the two-segment case equals the
     mixed mask, a hand-written golden mask, brute force through a second
     characterisation of the allowed keys, suffix-query consistency and
-    invariance under permutations inside an image block (tests/test_oracle_segments.py).
+    invariance under permutations inside an image block (tests/test_oracle_segments.py);
+  * key chunks and the log-sum-exp merge: merging the chunks of a partition
+    gives the pinned full attention, log-sum-exp equals scipy's and a
+    pure-Python one, empty chunks give (0, -inf) (tests/test_oracle_chunks.py).
 Nothing is "parity unpinned".
 """
 from .attention import (mixed_mask, masked_softmax, masked_attention, attention_probs,
@@ -28,7 +31,7 @@ from .attention import (mixed_mask, masked_softmax, masked_attention, attention_
                         padded_attention, unpad, useful_flops, offsets)
 from .brute import brute_packed_attention, allowed_keys, brute_segment_attention, segment_allowed_keys
 from .segments import (CAUSAL, FULL, SegSeq, make_seq, segment_mask, segment_attention,
-                       segment_attention_rows, segment_useful_flops)
+                       segment_attention_rows, segment_useful_flops, chunk_attention, merge_partials)
 from . import fp8
 
 __all__ = [
@@ -37,4 +40,5 @@ __all__ = [
     "useful_flops", "offsets", "brute_packed_attention", "allowed_keys", "fp8",
     "brute_segment_attention", "segment_allowed_keys", "CAUSAL", "FULL", "SegSeq", "make_seq",
     "segment_mask", "segment_attention", "segment_attention_rows", "segment_useful_flops",
+    "chunk_attention", "merge_partials",
 ]

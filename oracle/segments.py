@@ -132,3 +132,65 @@ def segment_useful_flops(seqs: Sequence[SegSeq], num_heads: int, head_dim: int) 
     for s in seqs:
         pairs += int(segment_mask(s.seg_len, s.seg_kind)[s.q_start:].sum())
     return 4 * int(head_dim) * int(num_heads) * pairs
+
+
+# ---------------------------------------------------------------------------
+# Key chunks, log-sum-exp and the merge of partial results (the single-GPU
+# half of Ring attention: "[RFC]: HunyuanImage 3.0 deployment", Proposed
+# Change P2, and the Parallelism Acceleration Guide's Ring-Attention, where
+# each rank holds one chunk of the keys and values and partial outputs are
+# combined through their log-sum-exp).
+
+def chunk_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, seqs: Sequence[SegSeq],
+                    k_lo: Sequence[int], k_hi: Sequence[int], scale: float):
+    """Attention of the queried rows over keys [k_lo_s, k_hi_s) of each sequence.
+
+    q [Nq, H, D] (queried rows), k, v [Nc, H, D] holding only each sequence's
+    chunk rows, packed in order. Returns (O fp64 [Nq, H, D], lse fp64 [Nq, H])
+    where lse = log(sum over allowed keys of the chunk of exp(scale q.k)),
+    -inf for a row with no allowed key there (its O row is zero).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    coff = offsets([int(b) - int(a) for a, b in zip(k_lo, k_hi)])
+    qoff = offsets([s.q_rows for s in seqs])
+    if k.shape[0] != coff[-1] or q.shape[0] != qoff[-1]:
+        raise ValueError("token counts do not match the chunks")
+    H = q.shape[1]
+    out = np.zeros_like(q)
+    lse = np.full((q.shape[0], H), -np.inf)
+    for si, s in enumerate(seqs):
+        lo, hi = int(k_lo[si]), int(k_hi[si])
+        if not 0 <= lo <= hi <= s.length:
+            raise ValueError("chunk must lie inside the sequence")
+        qa, qb, ca, cb = qoff[si], qoff[si + 1], coff[si], coff[si + 1]
+        if qb == qa or hi == lo:
+            continue
+        mask = segment_mask(s.seg_len, s.seg_kind)[s.q_start:, lo:hi]
+        for h in range(H):
+            out[qa:qb, h] = masked_attention(q[qa:qb, h], k[ca:cb, h], v[ca:cb, h], mask, scale)
+            sc = float(scale) * (q[qa:qb, h] @ k[ca:cb, h].T)
+            sc = np.where(mask, sc, -np.inf)
+            m = sc.max(axis=1)
+            ok = np.isfinite(m)
+            with np.errstate(invalid="ignore"):
+                tot = np.where(mask, np.exp(sc - np.where(ok, m, 0.0)[:, None]), 0.0).sum(axis=1)
+            lse[qa:qb, h] = np.where(ok, m + np.log(np.where(ok, tot, 1.0)), -np.inf)
+    return out, lse
+
+
+def merge_partials(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):
+    """Combine partial results over disjoint key sets:
+    lse = log(sum_c exp(lse_c)), O = sum_c exp(lse_c - lse) O_c; rows where
+    every part has lse = -inf give O = 0 and lse = -inf."""
+    o = np.stack([np.asarray(x, np.float64) for x in o_parts])      # [P, N, H, D]
+    l = np.stack([np.asarray(x, np.float64) for x in lse_parts])    # [P, N, H]
+    top = l.max(axis=0)
+    ok = np.isfinite(top)
+    with np.errstate(invalid="ignore"):
+        w = np.where(np.isfinite(l), np.exp(l - np.where(ok, top, 0.0)[None]), 0.0)
+    den = w.sum(axis=0)
+    lse = np.where(ok, top + np.log(np.where(ok, den, 1.0)), -np.inf)
+    out = np.where(ok[..., None], (w[..., None] * o).sum(axis=0) / np.where(ok, den, 1.0)[..., None], 0.0)
+    return out, lse
