@@ -24,7 +24,10 @@
  *
  * Generalization (pva_seg_desc_build_segments): a sequence may be any list of
  * text (causal) and image (full) segments, and only a suffix of it may be
- * queried, with Q and O holding just the queried rows.
+ * queried, with Q and O holding just the queried rows. With
+ * pva_seg_desc_build_kv_chunk, K and V may hold just a chunk of each
+ * sequence's keys; packed_attn_fwd_partial then also returns the rows'
+ * log-sum-exp and pva_merge_partials combines the chunks' results.
  *
  * Ownership: the caller owns every tensor and every stream. The library owns
  * only a pva_seg_desc (host copy + device work list), freed by
@@ -124,6 +127,28 @@ int pva_seg_desc_build_segments(const int32_t* seg_len, const int32_t* seg_kind,
                                 const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
                                 pva_dtype dtype, void* stream, pva_seg_desc** out);
 
+/*
+ * Key-chunk builder: as pva_seg_desc_build_segments, but k and v hold only
+ * the key rows [k_lo_s, k_hi_s) of each sequence (one rank's share of the
+ * keys in Ring attention, "[RFC]: HunyuanImage 3.0 deployment", Proposed
+ * Change P2; the Parallelism guide's Ring-Attention). cu_seqlens then
+ * counts those chunk rows. A queried row attends to the allowed keys of its
+ * mask row that fall in the chunk; a row with none gets O = 0 and
+ * lse = -inf from packed_attn_fwd_partial.
+ *   k_lo, k_hi : host int32 [nseq], 0 <= k_lo <= k_hi <= L_s
+ * Launched with packed_attn_fwd_partial (or the varlen entry points).
+ */
+int pva_seg_desc_build_kv_chunk(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi, int32_t nseq,
+                                int32_t num_heads, int32_t head_dim, pva_dtype dtype, void* stream,
+                                pva_seg_desc** out);
+
+/* Host-only planning of the key-chunk builder. */
+int pva_seg_desc_build_kv_chunk_host(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                     const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi,
+                                     int32_t nseq, int32_t num_heads, int32_t head_dim, pva_dtype dtype,
+                                     pva_seg_desc** out);
+
 /* Host-only planning of the general builder (inspection, no device). */
 int pva_seg_desc_build_segments_host(const int32_t* seg_len, const int32_t* seg_kind,
                                      const int32_t* seg_count, const int32_t* q_start, int32_t nseq,
@@ -139,9 +164,11 @@ int pva_seg_desc_cu_seqlens(const pva_seg_desc* desc, const int32_t** host_cu, i
  * q_start is 0. Valid until freed. */
 int pva_seg_desc_cu_seqlens_q(const pva_seg_desc* desc, const int32_t** host_cu_q, int32_t* len);
 
-/* Host view of the per-token key limits (int32 [N]): row i of sequence s
- * may attend to keys [0, lim) of that sequence, lim = key_limits[
- * cu_seqlens[s] + i]. Non-decreasing within a sequence. Valid until freed. */
+/* Host view of the key limits of the queried rows (int32 [total_q], in Q/O
+ * row order): queried row r of sequence s may attend to the K/V rows
+ * [0, lim) of that sequence held by k and v, lim = key_limits[r]
+ * (row q_start_s + r - cu_seqlens_q[s] of the sequence). Non-decreasing within
+ * a sequence. Valid until freed. */
 int pva_seg_desc_key_limits(const pva_seg_desc* desc, const int32_t** key_limits, int32_t* len);
 
 /* Useful multiply-add FLOPs over allowed (query, key) pairs of the queried
@@ -215,6 +242,35 @@ int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, cons
                                const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
                                void* out, void* stream);
+
+/*
+ * Partial forward for Ring-style combination (bf16 descriptors): writes O in
+ * fp32 (out_f32: device float [total_q, H, D], 16-byte aligned) and the
+ * log-sum-exp of every queried row's scaled scores over the keys it sees
+ * (lse: device float [total_q, H], index row * H + h, 4-byte aligned):
+ * lse = log(sum_j exp(scale * q.k_j)), -inf (and O = 0) for a row with no
+ * allowed key among the K/V rows held. Otherwise as packed_attn_fwd_varlen.
+ */
+int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                            float* out_f32, float* lse, void* stream);
+
+/*
+ * Merge of n_parts partial results over disjoint key sets (the combining
+ * step of Ring attention, Proposed Change P2): for each of `rows`
+ * (query, head) rows,
+ *   lse = log sum_c exp(lse_c),   O = sum_c exp(lse_c - lse) O_c;
+ * rows whose parts are all -inf give O = 0 and lse = -inf.
+ *   o_parts   : device float [n_parts, rows, head_dim], 16-byte aligned
+ *               (part c's O from packed_attn_fwd_partial is one [rows, D] slab)
+ *   lse_parts : device float [n_parts, rows], 4-byte aligned
+ *   n_parts   : >= 1; rows >= 0; head_dim in {64, 128}
+ *   out       : device bf16 [rows, head_dim], 16-byte aligned
+ *   lse_out   : device float [rows], or NULL
+ * Asynchronous on `stream`; allocates nothing.
+ */
+int pva_merge_partials(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows,
+                       int32_t head_dim, void* out, float* lse_out, void* stream);
 
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* pva_last_error(void);

@@ -32,7 +32,8 @@ EXPORTED = [
     "pva_seg_desc_build_segments_host", "pva_seg_desc_cu_seqlens", "pva_seg_desc_cu_seqlens_q",
     "pva_seg_desc_key_limits", "pva_seg_desc_useful_flops", "pva_seg_desc_tile", "pva_seg_desc_work_items",
     "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
-    "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version",
+    "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
+    "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials",
 ]
 
 
@@ -68,6 +69,16 @@ def lib() -> ctypes.CDLL:
     L.pva_seg_desc_build_segments_host.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
                                                    ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)]
     L.pva_seg_desc_build_segments_host.restype = ctypes.c_int
+    L.pva_seg_desc_build_kv_chunk.argtypes = [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build_kv_chunk.restype = ctypes.c_int
+    L.pva_seg_desc_build_kv_chunk_host.argtypes = [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)]
+    L.pva_seg_desc_build_kv_chunk_host.restype = ctypes.c_int
+    L.packed_attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
+    L.packed_attn_fwd_partial.restype = ctypes.c_int
+    L.pva_merge_partials.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
+    L.pva_merge_partials.restype = ctypes.c_int
     L.pva_seg_desc_cu_seqlens_q.argtypes = [vp, ctypes.POINTER(i32p), i32p]
     L.pva_seg_desc_cu_seqlens_q.restype = ctypes.c_int
     L.pva_seg_desc_key_limits.argtypes = [vp, ctypes.POINTER(i32p), i32p]
@@ -156,10 +167,11 @@ class SegDesc:
 
     @classmethod
     def segments(cls, seqs, num_heads: int, head_dim: int, dtype: str = "bf16", stream=None,
-                 host_only: bool = False) -> "SegDesc":
+                 host_only: bool = False, k_lo=None, k_hi=None) -> "SegDesc":
         """General descriptor. ``seqs``: one entry per sequence, each
         ``(seg_len, seg_kind)`` or ``(seg_len, seg_kind, q_start)`` with kinds
-        SEG_CAUSAL / SEG_FULL (objects with those attributes work too)."""
+        SEG_CAUSAL / SEG_FULL (objects with those attributes work too).
+        ``k_lo`` / ``k_hi`` (per sequence) restrict K/V to a key chunk."""
         if dtype not in DTYPES:
             raise PvaError(PVA_ERR_INVALID_ARG, f"dtype must be one of {sorted(DTYPES)}")
         lens, kinds, counts, starts = [], [], [], []
@@ -181,7 +193,21 @@ class SegDesc:
         ca, cp = _i32_array(counts)
         sa, sp = _i32_array(starts)
         h = ctypes.c_void_p()
-        if host_only:
+        if (k_lo is None) != (k_hi is None):
+            raise PvaError(PVA_ERR_INVALID_ARG, "give both k_lo and k_hi or neither")
+        if k_lo is not None:
+            if len(k_lo) != len(ca) or len(k_hi) != len(ca):
+                raise PvaError(PVA_ERR_INVALID_ARG, "one key chunk per sequence")
+            loa, lop = _i32_array(k_lo)
+            hia, hip_ = _i32_array(k_hi)
+            if host_only:
+                st = L.pva_seg_desc_build_kv_chunk_host(lp, kp, cp, sp, lop, hip_, len(ca), int(num_heads),
+                                                        int(head_dim), DTYPES[dtype], ctypes.byref(h))
+            else:
+                st = L.pva_seg_desc_build_kv_chunk(lp, kp, cp, sp, lop, hip_, len(ca), int(num_heads), int(head_dim),
+                                                   DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream)),
+                                                   ctypes.byref(h))
+        elif host_only:
             st = L.pva_seg_desc_build_segments_host(lp, kp, cp, sp, len(ca), int(num_heads), int(head_dim),
                                                     DTYPES[dtype], ctypes.byref(h))
         else:
@@ -354,6 +380,58 @@ def packed_attn_fwd_varlen_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q,
     st = lib().packed_attn_fwd_varlen_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
                                           _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), seg_desc.handle,
                                           ctypes.c_float(scale), _ptr(out), ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
+
+
+def packed_attn_fwd_partial(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDesc, scale: float, out_f32, lse,
+                            stream=None):
+    """bf16 forward writing fp32 O ([total_q, H, D]) and the rows' log-sum-exp
+    ([total_q, H]); returns (out_f32, lse)."""
+    import torch
+    Nq, H, D = seg_desc.total_q, seg_desc.num_heads, seg_desc.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        N = Nq if name == "q" else seg_desc.total_tokens
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 or tuple(t.shape) != (N, H, D)
+                or not t.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a contiguous device bf16 [{N}, {H}, {D}] tensor")
+    if (not isinstance(out_f32, torch.Tensor) or not out_f32.is_cuda or out_f32.dtype != torch.float32
+            or tuple(out_f32.shape) != (Nq, H, D) or not out_f32.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out_f32 must be a contiguous device float32 [{Nq}, {H}, {D}] tensor")
+    if (not isinstance(lse, torch.Tensor) or not lse.is_cuda or lse.dtype != torch.float32
+            or tuple(lse.shape) != (Nq, H) or not lse.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"lse must be a contiguous device float32 [{Nq}, {H}] tensor")
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                       seg_desc.handle, ctypes.c_float(scale), _ptr(out_f32), _ptr(lse),
+                                       ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out_f32, lse
+
+
+def merge_partials(o_parts, lse_parts, out, lse_out=None, stream=None):
+    """Combine partial results: o_parts float32 [P, rows..., D], lse_parts
+    float32 [P, rows...] (same leading shape), out bf16 [rows..., D];
+    optional lse_out float32 [rows...]. Returns out."""
+    import torch
+    if (not isinstance(o_parts, torch.Tensor) or not o_parts.is_cuda or o_parts.dtype != torch.float32
+            or not o_parts.is_contiguous() or o_parts.dim() < 2):
+        raise PvaError(PVA_ERR_INVALID_ARG, "o_parts must be a contiguous device float32 [P, ..., D] tensor")
+    P, D = o_parts.shape[0], o_parts.shape[-1]
+    rows = o_parts[0].numel() // D
+    if (not isinstance(lse_parts, torch.Tensor) or not lse_parts.is_cuda or lse_parts.dtype != torch.float32
+            or not lse_parts.is_contiguous() or lse_parts.numel() != P * rows or lse_parts.shape[0] != P):
+        raise PvaError(PVA_ERR_INVALID_ARG, "lse_parts must be a contiguous device float32 [P, rows] tensor")
+    if (not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.bfloat16 or not out.is_contiguous()
+            or out.numel() != rows * D):
+        raise PvaError(PVA_ERR_INVALID_ARG, "out must be a contiguous device bf16 tensor of rows x D elements")
+    if lse_out is not None and (not lse_out.is_cuda or lse_out.dtype != torch.float32 or lse_out.numel() != rows
+                                or not lse_out.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, "lse_out must be a contiguous device float32 tensor of rows elements")
+    st = lib().pva_merge_partials(_ptr(o_parts), _ptr(lse_parts), int(P), int(rows), int(D), _ptr(out),
+                                  _ptr(lse_out) if lse_out is not None else None,
+                                  ctypes.c_void_p(_stream_handle(stream)))
     _check(st)
     return out
 

@@ -14,7 +14,9 @@
 
 namespace pva {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, hipStream_t stream);
+                    float scale, void* out, int out_f32, float* lse, hipStream_t stream);
+int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int64_t rows, int head_dim, void* out,
+                 float* lse_out, hipStream_t stream);
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks,
                    const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, void* out,
                    hipStream_t stream);
@@ -136,23 +138,23 @@ int build_two(const int32_t* text_len, const int32_t* image_len, int32_t nseq, i
 }
 
 int build_segs(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count, const int32_t* q_start,
-               int32_t nseq, int32_t num_heads, int32_t head_dim, pva_dtype dtype, bool upload, void* stream,
-               pva_seg_desc** out) {
+               const int32_t* k_lo, const int32_t* k_hi, int32_t nseq, int32_t num_heads, int32_t head_dim,
+               pva_dtype dtype, bool upload, void* stream, pva_seg_desc** out) {
   return build_common(
       [&](pva::Plan* p, std::string* err) {
-        return pva::build_plan_segments(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, p,
-                                        err);
+        return pva::build_plan_segments(seg_len, seg_kind, seg_count, q_start, k_lo, k_hi, nseq, num_heads, head_dim,
+                                        dtype, p, err);
       },
       upload, stream, out);
 }
 
 int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-             const pva_seg_desc* d, float scale, void* out, void* stream) {
+             const pva_seg_desc* d, float scale, void* out, int out_f32, float* lse, void* stream) {
   int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_BF16);
   if (st != PVA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, s);
+  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, out_f32, lse, s);
   if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
   return ok();
 }
@@ -194,13 +196,32 @@ int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, i
 int pva_seg_desc_build_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
                                 const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
                                 pva_dtype dtype, void* stream, pva_seg_desc** out) {
-  return build_segs(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, true, stream, out);
+  return build_segs(seg_len, seg_kind, seg_count, q_start, nullptr, nullptr, nseq, num_heads, head_dim, dtype, true,
+                    stream, out);
 }
 
 int pva_seg_desc_build_segments_host(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
                                      const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
                                      pva_dtype dtype, pva_seg_desc** out) {
-  return build_segs(seg_len, seg_kind, seg_count, q_start, nseq, num_heads, head_dim, dtype, false, nullptr, out);
+  return build_segs(seg_len, seg_kind, seg_count, q_start, nullptr, nullptr, nseq, num_heads, head_dim, dtype, false,
+                    nullptr, out);
+}
+
+int pva_seg_desc_build_kv_chunk(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi, int32_t nseq,
+                                int32_t num_heads, int32_t head_dim, pva_dtype dtype, void* stream,
+                                pva_seg_desc** out) {
+  if (!k_lo || !k_hi) return set_error(PVA_ERR_INVALID_ARG, "k_lo / k_hi is NULL");
+  return build_segs(seg_len, seg_kind, seg_count, q_start, k_lo, k_hi, nseq, num_heads, head_dim, dtype, true, stream,
+                    out);
+}
+
+int pva_seg_desc_build_kv_chunk_host(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
+                                     const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi, int32_t nseq,
+                                     int32_t num_heads, int32_t head_dim, pva_dtype dtype, pva_seg_desc** out) {
+  if (!k_lo || !k_hi) return set_error(PVA_ERR_INVALID_ARG, "k_lo / k_hi is NULL");
+  return build_segs(seg_len, seg_kind, seg_count, q_start, k_lo, k_hi, nseq, num_heads, head_dim, dtype, false,
+                    nullptr, out);
 }
 
 int pva_seg_desc_cu_seqlens(const pva_seg_desc* d, const int32_t** host_cu, int32_t* len) {
@@ -256,13 +277,36 @@ int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const pva_seg_desc* seg_desc, float scale, void* out, void* stream) {
   int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  return fwd_bf16(q, k, v, cu_seqlens, cu_seqlens, seg_desc, scale, out, stream);
+  return fwd_bf16(q, k, v, cu_seqlens, cu_seqlens, seg_desc, scale, out, 0, nullptr, stream);
 }
 
 int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
                            void* stream) {
-  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, stream);
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, 0, nullptr, stream);
+}
+
+int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                            const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, float* out_f32,
+                            float* lse, void* stream) {
+  if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out_f32, 1, lse, stream);
+}
+
+int pva_merge_partials(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,
+                       void* out, float* lse_out, void* stream) {
+  if (!o_parts || !lse_parts || !out) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  if (n_parts < 1) return set_error(PVA_ERR_INVALID_ARG, "n_parts must be >= 1");
+  if (rows < 0) return set_error(PVA_ERR_INVALID_ARG, "rows must be >= 0");
+  if (head_dim != 64 && head_dim != 128) return set_error(PVA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (!aligned16(o_parts) || !aligned16(out)) return set_error(PVA_ERR_INVALID_ARG, "o_parts and out must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
+    return set_error(PVA_ERR_INVALID_ARG, "lse_parts and lse_out must be 4-byte aligned");
+  if (rows > (int64_t(1) << 40) / head_dim / n_parts) return set_error(PVA_ERR_INVALID_ARG, "tensor too large");
+  int st = pva::launch_merge(o_parts, lse_parts, n_parts, rows, head_dim, out, lse_out, static_cast<hipStream_t>(stream));
+  if (st != PVA_OK) return set_error(st, "merge kernel launch failed");
+  return ok();
 }
 
 int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
@@ -282,6 +326,6 @@ int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, cons
 
 const char* pva_last_error(void) { return g_last_error.c_str(); }
 
-const char* pva_version(void) { return "pva 0.2 gfx950"; }
+const char* pva_version(void) { return "pva 0.3 gfx950"; }
 
 }  // extern "C"

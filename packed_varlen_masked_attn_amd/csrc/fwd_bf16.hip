@@ -255,7 +255,8 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
                                                                     const int32_t* __restrict__ cu,
                                                                     const int32_t* __restrict__ lims,
                                                                     const WorkItem* __restrict__ items, int H,
-                                                                    float scale_log2, __bf16* __restrict__ O) {
+                                                                    float scale_log2, void* __restrict__ O,
+                                                                    int out_f32, float* __restrict__ lse) {
   using Kn = Kernel<D>;
   using Cfg = typename Kn::Cfg;
   using s16x8 = typename Kn::s16x8;
@@ -289,14 +290,16 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
   const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + base);
 
-  // this lane's query row and its key limit; rows past the sequence end see
-  // all L keys (their outputs are never stored). The limits never decrease
-  // along the rows, so the wave's first row has the smallest.
-  const int32_t* slim = lims + kseq;
+  // this lane's query row and its key limit; rows past the tile see all L
+  // keys held (their outputs are never stored). The limits are stored per
+  // queried row and never decrease along the rows, so the wave's first row
+  // has the smallest.
+  const int qend = it.q0 + it.q_rows;
+  const int32_t* slim = lims + (it.qo_row - it.q0);
   const int wrow0 = it.q0 + 32 * wave;
   const int qrow = wrow0 + l32;
-  const int mylim = qrow < L ? slim[qrow] : L;
-  const int wlim_min = wrow0 < L ? slim[wrow0] : L;
+  const int mylim = qrow < qend ? slim[qrow] : L;
+  const int wlim_min = wrow0 < qend ? slim[wrow0] : L;
   const int kend = it.k_end;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
@@ -325,7 +328,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   bf16x8 qf[NKC];
 #pragma unroll
   for (int c = 0; c < NKC; ++c) {
-    if (qrow < L)
+    if (qrow < qend)
       qf[c] = *reinterpret_cast<const bf16x8*>(Qh + int64_t(qrow) * rs + 16 * c + 8 * g);
     else
       qf[c] = bf16x8{};
@@ -355,6 +358,8 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
     sa = Kn::s_tile(kst[0], qf, ra);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
     st.m = Kn::tile_max(sa, scale_log2);  // first tile: O and l are still zero
+    // a row with no key in range keeps a finite reference (its p are all 0)
+    if (st.m == -INFINITY) st.m = 0.0f;
   }
 
   // Iteration j; `scur` holds S(j), `snext` receives S(j+1). SJ = j % NS
@@ -413,44 +418,62 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
     iteration(I3{}, j + 3, sb, sa);
   }
 
-  // ---- epilogue: O = O^T / l, bf16, rows of this sequence only
+  // ---- epilogue: O = O^T / l (bf16, or fp32 for partial results), rows of
+  // this tile only; optionally the row's log-sum-exp of the scaled scores,
+  // ln 2 * (m + log2 l) (-inf for a row with no key in range)
   const float lt = half_swap_sum(st.l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (qrow < L) {
-    __bf16* orow = O + qbase + int64_t(qrow) * rs;
+  if (qrow < qend) {
+    const int64_t orow = qbase + int64_t(qrow) * rs;
+    if (out_f32) {
+      float* o = static_cast<float*>(O) + orow;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 w;
+        for (int i4 = 0; i4 < 4; ++i4) {
+          f32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][4 * i4 + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * db + 8 * i4 + 4 * g) = w;
-      }
+          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * i4 + e] * inv;
+          *reinterpret_cast<f32x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
+        }
+    } else {
+      __bf16* o = static_cast<__bf16*>(O) + orow;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          bf16x4 w;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][4 * i4 + e] * inv);
+          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
+        }
+    }
+    if (lse && g == 0)
+      lse[int64_t(it.qo_row - it.q0 + qrow) * H + it.head] =
+          lt > 0.0f ? 0.6931471805599453f * (st.m + __log2f(lt)) : -INFINITY;
   }
 }
 
 template <int D>
 int launch(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d, float scale,
-           void* out, hipStream_t stream) {
+           void* out, int out_f32, float* lse, hipStream_t stream) {
   using Cfg = Bf16Cfg<D>;
   const int n = static_cast<int>(d->plan.items.size());
   if (n == 0) return PVA_OK;
   const float scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
   hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, static_cast<const __bf16*>(q),
                      static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu, d->d_lims,
-                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2,
-                     static_cast<__bf16*>(out));
+                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2, out, out_f32, lse);
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, hipStream_t stream) {
+                    float scale, void* out, int out_f32, float* lse, hipStream_t stream) {
   switch (d->plan.head_dim) {
-    case 64: return launch<64>(q, k, v, cu, d, scale, out, stream);
-    case 128: return launch<128>(q, k, v, cu, d, scale, out, stream);
+    case 64: return launch<64>(q, k, v, cu, d, scale, out, out_f32, lse, stream);
+    case 128: return launch<128>(q, k, v, cu, d, scale, out, out_f32, lse, stream);
     default: return PVA_ERR_UNSUPPORTED;
   }
 }

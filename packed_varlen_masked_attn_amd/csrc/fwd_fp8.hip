@@ -255,14 +255,15 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const float scale_log2 = q_scale[sh] * k_scale[sh] * scale_log2e;  // log2 units per raw score
   const float vs = v_scale[sh];
 
-  // this lane's query row and its key limit (rows past the end: L); the
-  // limits never decrease along the rows, so the wave's first row has the
-  // smallest
-  const int32_t* slim = lims + kseq;
+  // this lane's query row and its key limit (rows past the tile: L, the K/V
+  // rows held); the limits never decrease along the rows, so the wave's
+  // first row has the smallest. The limits are stored per queried row.
+  const int qend = it.q0 + it.q_rows;
+  const int32_t* slim = lims + (it.qo_row - it.q0);
   const int qrow = it.q0 + 32 * wave + l32;
-  const int mylim = qrow < L ? slim[qrow] : L;
+  const int mylim = qrow < qend ? slim[qrow] : L;
   const int wrow0 = it.q0 + 32 * wave;
-  const bool wave_active = wrow0 < L;
+  const bool wave_active = wrow0 < qend;
   const int wlim_min = wave_active ? slim[wrow0] : L;
   const int kend = it.k_end;
 
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   i32x8 qf[NKS];
 #pragma unroll
   for (int c = 0; c < NKS; ++c) {
-    if (qrow < L)
+    if (qrow < qend)
       qf[c] = *reinterpret_cast<const i32x8*>(Qh + int64_t(qrow) * rs + 64 * c + 32 * g);
     else
       qf[c] = i32x8{};
@@ -334,6 +335,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     s_mfma(sa, kst[0]);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
     m_run = Kn::tile_max(sa, scale_log2);
+    // a row with no key in range keeps a finite reference (its p are all 0)
+    if (m_run == -INFINITY) m_run = 0.0f;
   }
 
   auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[NB], f32x16(&snext)[NB]) {
@@ -388,7 +391,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   }
 
   // ---- epilogue: O = O^T * v_s / l (l from the ones block), bf16
-  if (wave_active && qrow < L) {
+  if (wave_active && qrow < qend) {
     const float lt = oacc[NDB][0];
     const float inv = lt > 0.0f ? vs / lt : 0.0f;
     __bf16* orow = O + qbase + int64_t(qrow) * rs;

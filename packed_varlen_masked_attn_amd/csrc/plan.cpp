@@ -17,6 +17,11 @@
 // Queries may cover only a suffix [q_start, L) of a sequence (the prefix's
 // keys and values are reused; Model structure item 1, the single Prefix KV):
 // query tiles then start at q_start and Q / O hold only the queried rows.
+//
+// K / V may hold only a chunk [k_lo, k_hi) of each sequence's keys (one
+// rank's share in Ring attention, Proposed Change P2): each queried row's
+// key limit is then taken relative to the chunk and clamped to [0, chunk
+// length]; a row whose limit is 0 has no key in the chunk.
 
 #include <algorithm>
 #include <cmath>
@@ -49,6 +54,7 @@ struct Group {  // all query tiles of one (sequence, head)
 struct SeqSpec {
   std::vector<int32_t> seg_len, seg_kind;
   int32_t q_start = 0;
+  int32_t k_lo = 0, k_hi = -1;  // key rows held by K/V; k_hi < 0: to the end
 };
 
 int check_shape(int32_t nseq, int32_t num_heads, int32_t head_dim, pva_dtype dtype, std::string* err) {
@@ -73,6 +79,8 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
   p.tile = tile_shape(dtype, head_dim);
   p.seq_len.resize(nseq);
   p.q_start.resize(nseq);
+  p.k_lo.resize(nseq);
+  p.kv_len.resize(nseq);
   p.cu_seqlens.assign(nseq + 1, 0);
   p.cu_seqlens_q.assign(nseq + 1, 0);
   int64_t total = 0, total_q = 0, pairs = 0;
@@ -81,37 +89,51 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
     for (int32_t n : seqs[s].seg_len) L += n;
     if (L < 1) return fail(err, PVA_ERR_INVALID_ARG, "every sequence needs at least one token");
     if (L > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "sequence too long");
-    // the kernels address one head's rows of a sequence with 32-bit byte
-    // offsets below 2^31 (row stride H * D elements of at most 2 bytes)
-    if (L * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
-      return fail(err, PVA_ERR_UNSUPPORTED, "sequence too long for 32-bit head addressing (L * H * D * 2 >= 2^31)");
     const int32_t qs = seqs[s].q_start;
     if (qs < 0 || qs > L) return fail(err, PVA_ERR_INVALID_ARG, "q_start must lie in [0, L]");
-    total += L;
+    const int64_t lo = seqs[s].k_lo, hi = seqs[s].k_hi < 0 ? L : seqs[s].k_hi;
+    if (lo < 0 || lo > hi || hi > L) return fail(err, PVA_ERR_INVALID_ARG, "key chunk must satisfy 0 <= k_lo <= k_hi <= L");
+    const int64_t Lk = hi - lo;
+    // the kernels address one head's rows of a sequence with 32-bit byte
+    // offsets below 2^31 (row stride H * D elements of at most 2 bytes)
+    if (Lk * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
+      return fail(err, PVA_ERR_UNSUPPORTED, "sequence too long for 32-bit head addressing (L * H * D * 2 >= 2^31)");
+    total += Lk;
     total_q += L - qs;
-    if (total > INT32_MAX) return fail(err, PVA_ERR_INVALID_ARG, "packed token count exceeds int32");
+    if (total > INT32_MAX || total_q > INT32_MAX)
+      return fail(err, PVA_ERR_INVALID_ARG, "packed token count exceeds int32");
     p.seq_len[s] = static_cast<int32_t>(L);
     p.q_start[s] = qs;
+    p.k_lo[s] = static_cast<int32_t>(lo);
+    p.kv_len[s] = static_cast<int32_t>(Lk);
     p.cu_seqlens[s + 1] = static_cast<int32_t>(total);
     p.cu_seqlens_q[s + 1] = static_cast<int32_t>(total_q);
   }
   // element offsets are formed as (token * H + h) * D in int64 on the device
-  if (total * int64_t(num_heads) * head_dim > (int64_t(1) << 62))
+  if (std::max(total, total_q) * int64_t(num_heads) * head_dim > (int64_t(1) << 62))
     return fail(err, PVA_ERR_INVALID_ARG, "tensor too large");
   p.total_tokens = total;
   p.total_q = total_q;
 
-  // ---- key limits: lim(i) = i + 1 in a text segment, the block's end in an image block
-  p.key_lim.resize(static_cast<size_t>(total));
+  // ---- key limits of the queried rows, in the coordinates of the K/V rows
+  // held: lim(i) = i + 1 in a text segment, the block's end in an image
+  // block, then shifted by k_lo and clamped to [0, kv_len]
+  p.key_lim.resize(static_cast<size_t>(total_q));
+  std::vector<int32_t> lim;
   for (int32_t s = 0; s < nseq; ++s) {
-    int32_t* lim = p.key_lim.data() + p.cu_seqlens[s];
+    lim.assign(p.seq_len[s], 0);
     int32_t a = 0;
     for (size_t g = 0; g < seqs[s].seg_len.size(); ++g) {
       const int32_t b = a + seqs[s].seg_len[g];
       for (int32_t i = a; i < b; ++i) lim[i] = seqs[s].seg_kind[g] == PVA_SEG_CAUSAL ? i + 1 : b;
       a = b;
     }
-    for (int32_t i = p.q_start[s]; i < p.seq_len[s]; ++i) pairs += lim[i];
+    int32_t* out = p.key_lim.data() + p.cu_seqlens_q[s];
+    for (int32_t i = p.q_start[s]; i < p.seq_len[s]; ++i) {
+      const int32_t c = std::min(std::max(lim[i] - p.k_lo[s], 0), p.kv_len[s]);
+      out[i - p.q_start[s]] = c;
+      pairs += c;
+    }
   }
   p.useful_flops = 4 * int64_t(head_dim) * num_heads * pairs;
 
@@ -120,7 +142,7 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
   std::vector<std::vector<WorkItem>> seq_tiles(nseq);
   for (int32_t s = 0; s < nseq; ++s) {
     const int32_t L = p.seq_len[s], qs = p.q_start[s];
-    const int32_t* lim = p.key_lim.data() + p.cu_seqlens[s];
+    const int32_t* qlim = p.key_lim.data() + p.cu_seqlens_q[s] - qs;  // indexed by row of the sequence
     for (int32_t qa = qs; qa < L; qa += BM) {
       const int32_t qb = std::min(qa + BM, L);
       WorkItem w;
@@ -128,10 +150,10 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
       w.head = 0;
       w.q0 = qa;
       w.q_rows = qb - qa;
-      w.k_full_end = lim[qa] / BN;
-      w.k_end = (lim[qb - 1] + BN - 1) / BN;
+      w.k_full_end = qlim[qa] / BN;
+      w.k_end = (qlim[qb - 1] + BN - 1) / BN;
       w.qo_row = p.cu_seqlens_q[s] + (qa - qs);
-      w.seq_len = L;
+      w.seq_len = p.kv_len[s];
       seq_tiles[s].push_back(w);
     }
   }
@@ -206,8 +228,8 @@ int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, 
 }
 
 int build_plan_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
-                        const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
-                        pva_dtype dtype, Plan* plan, std::string* err) {
+                        const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi, int32_t nseq,
+                        int32_t num_heads, int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err) {
   if (!plan) return fail(err, PVA_ERR_INVALID_ARG, "plan output is NULL");
   if (!seg_len || !seg_kind || !seg_count) return fail(err, PVA_ERR_INVALID_ARG, "a segment array is NULL");
   int st = check_shape(nseq, num_heads, head_dim, dtype, err);
@@ -227,6 +249,13 @@ int build_plan_segments(const int32_t* seg_len, const int32_t* seg_kind, const i
       seqs[s].seg_kind.push_back(seg_kind[g]);
     }
     seqs[s].q_start = q_start ? q_start[s] : 0;
+    if ((k_lo == nullptr) != (k_hi == nullptr))
+      return fail(err, PVA_ERR_INVALID_ARG, "k_lo and k_hi must both be given or both be NULL");
+    if (k_lo) {
+      if (k_hi[s] < 0) return fail(err, PVA_ERR_INVALID_ARG, "key chunk must satisfy 0 <= k_lo <= k_hi <= L");
+      seqs[s].k_lo = k_lo[s];
+      seqs[s].k_hi = k_hi[s];
+    }
   }
   return plan_sequences(seqs, num_heads, head_dim, dtype, plan, err);
 }

@@ -26,7 +26,7 @@ struct WorkItem {
   int32_t k_full_end;
   int32_t k_end;
   int32_t qo_row;  // row of Q and O holding query row q0 (packed queried rows)
-  int32_t seq_len;
+  int32_t seq_len; // K/V rows held for this sequence (its length unless chunked)
 };
 static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 
@@ -56,25 +56,32 @@ struct Plan {
   int32_t nseq = 0, num_heads = 0, head_dim = 0;
   TileShape tile{0, 0};
   std::vector<int32_t> text_len, image_len;  // two-segment builds only (for inspection)
-  std::vector<int32_t> seq_len, q_start;     // per sequence
-  std::vector<int32_t> cu_seqlens;           // K/V token offsets [nseq + 1]
+  std::vector<int32_t> seq_len, q_start;     // per sequence: length, first queried row
+  std::vector<int32_t> k_lo, kv_len;         // per sequence: first key row held by K/V, rows held
+  std::vector<int32_t> cu_seqlens;           // K/V row offsets [nseq + 1]
   std::vector<int32_t> cu_seqlens_q;         // Q/O row offsets [nseq + 1] (equal when q_start == 0)
-  std::vector<int32_t> key_lim;              // per K/V token: allowed keys of that row are [0, lim)
+  std::vector<int32_t> key_lim;              // per queried row: allowed K/V rows are [0, lim) of its sequence
   std::vector<WorkItem> items;               // launch order, XCD-interleaved, padded with empty slots
   int64_t useful_flops = 0;
-  int64_t total_tokens = 0;
-  int64_t total_q = 0;
-  bool queries_suffix() const { return total_q != total_tokens; }
+  int64_t total_tokens = 0;  // K/V rows
+  int64_t total_q = 0;       // Q/O rows
+  bool queries_suffix() const { return total_q != total_tokens || chunked(); }
+  bool chunked() const {
+    for (size_t s = 0; s < kv_len.size(); ++s)
+      if (k_lo[s] != 0 || kv_len[s] != seq_len[s]) return true;
+    return false;
+  }
 };
 
 // Validates and plans; on failure returns a status and fills `err`.
 // Two segments per sequence: text (causal) then one image block (full).
 int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err);
-// Any number of segments per sequence and an optional first queried row.
+// Any number of segments per sequence, an optional first queried row and an
+// optional key chunk [k_lo, k_hi) held by K/V (both NULL: whole sequences).
 int build_plan_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
-                        const int32_t* q_start, int32_t nseq, int32_t num_heads, int32_t head_dim,
-                        pva_dtype dtype, Plan* plan, std::string* err);
+                        const int32_t* q_start, const int32_t* k_lo, const int32_t* k_hi, int32_t nseq,
+                        int32_t num_heads, int32_t head_dim, pva_dtype dtype, Plan* plan, std::string* err);
 
 }  // namespace pva
 

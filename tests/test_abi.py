@@ -191,3 +191,24 @@ def test_new_accessor_null_args():
     assert L.pva_seg_desc_cu_seqlens_q(None, None, None) == pva.PVA_ERR_INVALID_ARG
     assert L.pva_seg_desc_key_limits(None, None, None) == pva.PVA_ERR_INVALID_ARG
     assert L.pva_seg_desc_build_segments_host(None, None, None, None, 1, 1, 64, 0, None) == pva.PVA_ERR_INVALID_ARG
+
+
+def test_partial_and_merge_reject_on_host():
+    L = pva.lib()
+    p = ctypes.c_void_p(FAKE)
+    desc = pva.SegDesc.segments([([8, 8], [0, 1])], 2, 64, host_only=True, k_lo=[0], k_hi=[8])
+    assert L.packed_attn_fwd_partial(p, p, p, p, p, desc.handle, ctypes.c_float(0.1), p, None, None) == \
+        pva.PVA_ERR_INVALID_ARG  # NULL lse
+    assert L.packed_attn_fwd_partial(p, p, p, p, p, desc.handle, ctypes.c_float(0.1), p, p, None) == \
+        pva.PVA_ERR_INVALID_ARG  # host-only descriptor
+    assert "host-only" in L.pva_last_error().decode()
+    # merge: NULL, counts, head size, alignment
+    assert L.pva_merge_partials(None, p, 2, 10, 128, p, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_merge_partials(p, p, 0, 10, 128, p, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_merge_partials(p, p, 2, -1, 128, p, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_merge_partials(p, p, 2, 10, 96, p, None, None) == pva.PVA_ERR_UNSUPPORTED
+    assert L.pva_merge_partials(ctypes.c_void_p(FAKE + 4), p, 2, 10, 128, p, None, None) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_merge_partials(p, ctypes.c_void_p(FAKE + 2), 2, 10, 128, p, None, None) == pva.PVA_ERR_INVALID_ARG
+    # a chunked descriptor cannot go through the whole-sequence entry point
+    d2 = pva.SegDesc.segments([([8, 8], [0, 1])], 2, 64, host_only=True, k_lo=[4], k_hi=[8])
+    assert L.packed_attn_fwd(p, p, p, p, d2.handle, ctypes.c_float(0.1), p, None) == pva.PVA_ERR_INVALID_ARG

@@ -142,8 +142,8 @@ def _check_plan_segments(seqs, H, D, dtype="bf16"):
     lims = desc.key_limits
     cu, cuq = desc.cu_seqlens, desc.cu_seqlens_q
     masks = [oracle.segment_mask(s.seg_len, s.seg_kind) for s in seqs]
-    for si, m in enumerate(masks):
-        assert lims[cu[si]:cu[si + 1]].tolist() == m.sum(axis=1).tolist()
+    for si, (m, s) in enumerate(zip(masks, seqs)):
+        assert lims[cuq[si]:cuq[si + 1]].tolist() == m[s.q_start:].sum(axis=1).tolist()
     items = desc.work_items
     real = items[items[:, 0] >= 0]
     seen = set()
@@ -231,3 +231,55 @@ def test_segments_q_start_at_end_has_no_items():
     items = d.work_items
     assert set(items[items[:, 0] >= 0][:, 0].tolist()) == {1}
     assert d.cu_seqlens_q.tolist() == [0, 0, 2]
+
+
+# ---- key chunks: K/V hold keys [k_lo, k_hi) of each sequence
+def _check_plan_chunk(seqs, k_lo, k_hi, H, D):
+    desc = pva.SegDesc.segments(seqs, H, D, host_only=True, k_lo=k_lo, k_hi=k_hi)
+    BM, BN = desc.tile
+    assert desc.cu_seqlens.tolist() == oracle.offsets([b - a for a, b in zip(k_lo, k_hi)]).tolist()
+    cuq = desc.cu_seqlens_q
+    lims = desc.key_limits
+    pairs = 0
+    masks = []
+    for si, s in enumerate(seqs):
+        m = oracle.segment_mask(s.seg_len, s.seg_kind)[:, k_lo[si]:k_hi[si]]
+        masks.append(m)
+        assert lims[cuq[si]:cuq[si + 1]].tolist() == m[s.q_start:].sum(axis=1).tolist()
+        pairs += int(m[s.q_start:].sum())
+    assert desc.useful_flops == 4 * D * H * pairs
+    items = desc.work_items
+    seen = set()
+    for seq, head, q0, q_rows, kfe, ke, qo_row, Lk in items[items[:, 0] >= 0].tolist():
+        s = seqs[seq]
+        seen.add((seq, head, q0))
+        assert Lk == k_hi[seq] - k_lo[seq] and qo_row == cuq[seq] + q0 - s.q_start
+        m = masks[seq][q0:q0 + q_rows]
+        n_kt = (Lk + BN - 1) // BN
+        cls = []
+        for kt in range(n_kt):
+            blk = m[:, kt * BN:(kt + 1) * BN]
+            cls.append("F" if (blk.all() and blk.shape[1] == BN) else ("P" if blk.any() else "S"))
+        assert _desc_classes(kfe, ke, Lk, BN) == tuple(cls)
+    assert seen == {(si, h, q0) for si, s in enumerate(seqs) for h in range(H) for q0 in range(s.q_start, s.length, BM)}
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_plan_kv_chunks_random(seed):
+    rng = np.random.default_rng(1700 + seed)
+    seqs = _random_segment_seqs(rng, int(rng.integers(1, 4)))
+    lo, hi = [], []
+    for s in seqs:
+        a, b = sorted(int(x) for x in rng.integers(0, s.length + 1, 2))
+        lo.append(a)
+        hi.append(b)
+    _check_plan_chunk(seqs, lo, hi, int(rng.integers(1, 3)), 128)
+
+
+def test_kv_chunk_rejects():
+    seqs = [([3, 5], [0, 1])]
+    for lo, hi in (([-1], [4]), ([5], [4]), ([0], [9])):
+        with pytest.raises(pva.PvaError):
+            pva.SegDesc.segments(seqs, 2, 64, host_only=True, k_lo=lo, k_hi=hi)
+    with pytest.raises(pva.PvaError):
+        pva.SegDesc.segments(seqs, 2, 64, host_only=True, k_lo=[0], k_hi=None)
