@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--kernel-only", action="store_true", help="time the kernel only (for profilers)")
+    ap.add_argument("--split-keys", type=int, default=1,
+                    help="P > 1: split every sequence's keys into P equal chunks; one step is P partial launches "
+                         "(fp32 O + log-sum-exp) and one merge (two-segment bf16 workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -229,6 +232,10 @@ def main():
     flops = desc.useful_flops
     stream = torch.cuda.current_stream()
 
+    if args.split_keys > 1:
+        split_keys_bench(args, w, q, k, v, scale, flops, desc_us)
+        return
+
     def step():
         if segmented and is_fp8:
             pva.packed_attn_fwd_varlen_fp8(q, k, v, qsd, ksd, vsd, cuq, cu, desc, scale, out, stream)
@@ -335,6 +342,78 @@ def main():
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, out, scale, args.cpu_seconds, is_fp8,
                                               (qs, ks, vs) if is_fp8 else None)
     print(json.dumps(result), flush=True)
+
+
+def split_keys_bench(args, w, q, k, v, scale, flops, desc_us):
+    """Ring attention's single-GPU half on the workload: each sequence's keys
+    split into P equal chunks (their K/V copied apart beforehand, as a rank
+    would hold them), one partial launch per chunk, then one merge."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    if isinstance(w, workloads.SegWorkload) or w.dtype == "fp8":
+        sys.exit("--split-keys runs the two-segment bf16 workloads")
+    P, dev, H, D = args.split_keys, q.device, w.num_heads, w.head_dim
+    seqs = [([t, i], [0, 1]) for t, i in zip(w.text_len, w.image_len)]
+    off = np.cumsum([0] + list(w.seq_len))
+    parts = []
+    for p in range(P):
+        lo = [L * p // P for L in w.seq_len]
+        hi = [L * (p + 1) // P for L in w.seq_len]
+        d = pva.SegDesc.segments(seqs, H, D, "bf16", k_lo=lo, k_hi=hi)
+        idx = torch.from_numpy(np.concatenate([np.arange(off[s] + a, off[s] + b) for s, (a, b) in
+                                               enumerate(zip(lo, hi))]).astype(np.int64)).to(dev)
+        parts.append((d, k.index_select(0, idx).contiguous(), v.index_select(0, idx).contiguous(),
+                      torch.from_numpy(d.cu_seqlens).to(dev)))
+    cuq = torch.from_numpy(parts[0][0].cu_seqlens_q).to(dev)
+    N = w.total_tokens
+    o_parts = torch.empty((P, N, H, D), dtype=torch.float32, device=dev)
+    l_parts = torch.empty((P, N, H), dtype=torch.float32, device=dev)
+    out = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for p, (d, kp, vp, cuk) in enumerate(parts):
+            pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, o_parts[p], l_parts[p], stream)
+        if ev is not None:
+            ev.record(stream)
+        pva.merge_partials(o_parts, l_parts, out, None, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t1s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    t_wall0 = time.perf_counter()
+    for i in range(args.steps):
+        t0s[i].record(stream)
+        step(mids[i])
+        t1s[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    part_ms = statistics.fmean(a.elapsed_time(b) for a, b in zip(t0s, mids))
+    merge_ms = statistics.fmean(a.elapsed_time(b) for a, b in zip(mids, t1s))
+    ms_per_step = wall * 1e3 / args.steps
+    value = flops * args.steps / wall / 1e12
+    merge_bytes = N * H * (P * (4 * D + 4) + 2 * D)
+    log(f"[bench] split keys x{P}: {ms_per_step:.4f} ms/step (partials {part_ms:.4f} ms, merge {merge_ms:.4f} ms) "
+        f"-> {value:.1f} useful TFLOP/s; merge {merge_bytes / merge_ms / 1e6:.0f} GB/s")
+    achieved = flops / (part_ms * 1e-3) / 1e12
+    print(json.dumps({
+        "metric": "useful attention TFLOP/s, key-split partials + merge (Ring attention's single-GPU half)",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
+        "config": {"workload": w.name, "split_keys": P, "text_len": list(w.text_len), "image_len": list(w.image_len),
+                   "num_heads": H, "head_dim": D, "parallelism": "single GPU"},
+        "partials_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5), "desc_build_us": round(desc_us, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
+                     "kernel": f"fwd_bf16_kernel<{D}> (all partial launches)"},
+        "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / merge_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                           "unit": "GB/s", "frac": round(merge_bytes / merge_ms / 1e6 / PEAK_HBM_GBS, 4),
+                           "traffic": None, "algorithmic_bytes": merge_bytes, "kernel": f"merge_kernel<{D}>"},
+    }), flush=True)
 
 
 def padded_baseline(w, q, k, v, scale, steps, flops, packed_ms):
