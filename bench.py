@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--kernel-only", action="store_true", help="time the kernel only (for profilers)")
+    ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
+                    help="bf16: K/V scattered over a block pool of BLOCK-row blocks in random order, read through "
+                         "a block table (packed_attn_fwd_paged)")
     ap.add_argument("--split-keys", type=int, default=1,
                     help="P > 1: split every sequence's keys into P equal chunks; one step is P partial launches "
                          "(fp32 O + log-sum-exp) and one merge (two-segment bf16 workloads)")
@@ -236,8 +239,36 @@ def main():
         split_keys_bench(args, w, q, k, v, scale, flops, desc_us)
         return
 
+    if args.paged:
+        if is_fp8:
+            sys.exit("--paged runs the bf16 workloads")
+        bs = args.paged
+        nblk = [(L + bs - 1) // bs for L in w.seq_len]
+        rng = np.random.default_rng(0)
+        order = torch.from_numpy(rng.permutation(sum(nblk)).astype(np.int64))
+        table = torch.full((w.nseq, max(nblk)), -1, dtype=torch.int32)
+        rows = torch.zeros(sum(nblk) * bs, dtype=torch.int64)  # pool row -> packed K/V row (padding rows: row 0)
+        a, used = 0, 0
+        for s_, L in enumerate(w.seq_len):
+            for b in range(nblk[s_]):
+                blk = int(order[used])
+                used += 1
+                table[s_, b] = blk
+                n = min(L, (b + 1) * bs) - b * bs
+                rows[blk * bs: blk * bs + n] = torch.arange(a + b * bs, a + b * bs + n)
+            a += L
+        ridx = rows.to(dev)
+        k_pool = k.index_select(0, ridx).view(sum(nblk), bs, H, D)
+        v_pool = v.index_select(0, ridx).view(sum(nblk), bs, H, D)
+        table = table.to(dev)
+        del k, v
+        torch.cuda.empty_cache()
+        log(f"[bench] paged K/V: {sum(nblk)} blocks of {bs} rows")
+
     def step():
-        if segmented and is_fp8:
+        if args.paged:
+            pva.packed_attn_fwd_paged(q, k_pool, v_pool, table, cuq, desc, scale, out, stream)
+        elif segmented and is_fp8:
             pva.packed_attn_fwd_varlen_fp8(q, k, v, qsd, ksd, vsd, cuq, cu, desc, scale, out, stream)
         elif segmented:
             pva.packed_attn_fwd_varlen(q, k, v, cuq, cu, desc, scale, out, stream)
@@ -290,6 +321,7 @@ def main():
             "head_dim": D,
             "tile": list(desc.tile),
             "parallelism": "single GPU",
+            **({"paged_block_rows": args.paged} if args.paged else {}),
         },
         "pct_of_bf16_peak": round(100.0 * value / PEAK_TFLOPS["bf16"], 2),
         "useful_flop_per_step": flops,
@@ -306,8 +338,8 @@ def main():
         "peak": PEAK_TFLOPS[dtype],
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
-        "traffic": stored_traffic(dtype, w.name),
-        "kernel": "fwd_fp8_kernel<128>" if is_fp8 else f"fwd_bf16_kernel<{D}>",
+        "traffic": None if args.paged else stored_traffic(dtype, w.name),
+        "kernel": ("fwd_fp8_kernel<128>" if is_fp8 else f"fwd_bf16_kernel<{D}>") + (" (paged K/V)" if args.paged else ""),
         "algorithmic_bytes": algorithmic_bytes(w),
     }
     if args.kernel_only:
@@ -333,6 +365,9 @@ def main():
         log(f"[bench] cold median {cmed:.4f} ms -> {result['cold']['tflops']} TFLOP/s")
 
     # ---------------- padded-mask baseline: pad to Lmax + explicit (B,1,Lmax,Lmax) bool mask + SDPA
+    if args.paged:
+        print(json.dumps(result), flush=True)
+        return
     if not args.no_padded and not is_fp8 and not segmented:
         result["padded_sdpa"] = padded_baseline(w, q, k, v, scale, args.padded_steps, flops, ms_per_step)
     torch.cuda.synchronize()

@@ -256,6 +256,32 @@ int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const i
                             float* out_f32, float* lse, void* stream);
 
 /*
+ * Forward with K and V in a paged pool (the scheduler-managed paged KV mode
+ * of "HunyuanImage-3.0-Instruct DiT Image Generation on 4x GPU", section
+ * "Scheduler-managed paged KV": unquantised bf16 K/V in a fixed physical
+ * pool, one logical row per CFG branch):
+ *   k_pool, v_pool : device bf16 [num_blocks, block_size, H, D], 16-byte aligned
+ *   block_table    : device int32 [nseq * table_stride]; key rows
+ *                    [b * block_size, (b + 1) * block_size) of sequence s live
+ *                    in pool block block_table[s * table_stride + b]
+ *   table_stride   : >= ceil(L_s / block_size) for every sequence
+ *   block_size     : a power of two, >= 32 (the key tile) and <= 2^20
+ *   num_blocks     : blocks in each pool (>= 1); entries outside [0, num_blocks)
+ *                    are clamped into the pool by the kernel (garbage in,
+ *                    garbage out, but no access outside the pool); with
+ *                    PVA_CHECK=1 the table is checked on the host first
+ *   q, out, cu_seqlens_q, seg_desc : as packed_attn_fwd_varlen (bf16, whole
+ *                    sequences: a descriptor from pva_seg_desc_build or
+ *                    pva_seg_desc_build_segments, any q_start)
+ * Pool rows past a sequence's end are never read into the result (they are
+ * zero-filled in the kernel), so partly used blocks need no clearing.
+ */
+int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          int32_t table_stride, int32_t block_size, int32_t num_blocks,
+                          const int32_t* cu_seqlens_q, const pva_seg_desc* seg_desc, float scale, void* out,
+                          void* stream);
+
+/*
  * Merge of n_parts partial results over disjoint key sets (the combining
  * step of Ring attention, Proposed Change P2): for each of `rows`
  * (query, head) rows,

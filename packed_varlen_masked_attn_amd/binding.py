@@ -33,7 +33,7 @@ EXPORTED = [
     "pva_seg_desc_key_limits", "pva_seg_desc_useful_flops", "pva_seg_desc_tile", "pva_seg_desc_work_items",
     "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
     "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
-    "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials",
+    "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials", "packed_attn_fwd_paged",
 ]
 
 
@@ -55,56 +55,43 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m packed_varlen_masked_attn_amd.build` (there is no fallback path)")
     L = ctypes.CDLL(LIB_PATH)
+
+    def sig(name, argtypes, restype):
+        if hasattr(L, name):  # an older build may lack newer entry points: calling them then fails loudly
+            f = getattr(L, name)
+            f.argtypes = argtypes
+            f.restype = restype
     i32p = ctypes.POINTER(ctypes.c_int32)
     vp = ctypes.c_void_p
-    L.pva_seg_desc_build.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
-                                     vp, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build.restype = ctypes.c_int
-    L.pva_seg_desc_build_host.argtypes = [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                                          ctypes.c_int, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build_host.restype = ctypes.c_int
-    L.pva_seg_desc_build_segments.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
-                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build_segments.restype = ctypes.c_int
-    L.pva_seg_desc_build_segments_host.argtypes = [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
-                                                   ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build_segments_host.restype = ctypes.c_int
-    L.pva_seg_desc_build_kv_chunk.argtypes = [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
-                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build_kv_chunk.restype = ctypes.c_int
-    L.pva_seg_desc_build_kv_chunk_host.argtypes = [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32,
-                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)]
-    L.pva_seg_desc_build_kv_chunk_host.restype = ctypes.c_int
-    L.packed_attn_fwd_partial.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp]
-    L.packed_attn_fwd_partial.restype = ctypes.c_int
-    L.pva_merge_partials.argtypes = [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp]
-    L.pva_merge_partials.restype = ctypes.c_int
-    L.pva_seg_desc_cu_seqlens_q.argtypes = [vp, ctypes.POINTER(i32p), i32p]
-    L.pva_seg_desc_cu_seqlens_q.restype = ctypes.c_int
-    L.pva_seg_desc_key_limits.argtypes = [vp, ctypes.POINTER(i32p), i32p]
-    L.pva_seg_desc_key_limits.restype = ctypes.c_int
-    L.pva_seg_desc_cu_seqlens.argtypes = [vp, ctypes.POINTER(i32p), i32p]
-    L.pva_seg_desc_cu_seqlens.restype = ctypes.c_int
-    L.pva_seg_desc_useful_flops.argtypes = [vp]
-    L.pva_seg_desc_useful_flops.restype = ctypes.c_int64
-    L.pva_seg_desc_tile.argtypes = [vp, i32p, i32p]
-    L.pva_seg_desc_tile.restype = ctypes.c_int
-    L.pva_seg_desc_work_items.argtypes = [vp, ctypes.POINTER(i32p), i32p]
-    L.pva_seg_desc_work_items.restype = ctypes.c_int
-    L.pva_seg_desc_free.argtypes = [vp]
-    L.pva_seg_desc_free.restype = None
-    L.packed_attn_fwd.argtypes = [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
-    L.packed_attn_fwd.restype = ctypes.c_int
-    L.packed_attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
-    L.packed_attn_fwd_fp8.restype = ctypes.c_int
-    L.packed_attn_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
-    L.packed_attn_fwd_varlen.restype = ctypes.c_int
-    L.packed_attn_fwd_varlen_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp]
-    L.packed_attn_fwd_varlen_fp8.restype = ctypes.c_int
-    L.pva_last_error.argtypes = []
-    L.pva_last_error.restype = ctypes.c_char_p
-    L.pva_version.argtypes = []
-    L.pva_version.restype = ctypes.c_char_p
+    sig("pva_seg_desc_build", [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                     vp, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_host", [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_segments", [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_segments_host", [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_kv_chunk", [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
+                                              ctypes.c_int32, ctypes.c_int, vp, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_kv_chunk_host", [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32,
+                                                   ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("packed_attn_fwd_partial", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_paged", [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                        ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("pva_merge_partials", [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp], ctypes.c_int)
+    sig("pva_seg_desc_cu_seqlens_q", [vp, ctypes.POINTER(i32p), i32p], ctypes.c_int)
+    sig("pva_seg_desc_key_limits", [vp, ctypes.POINTER(i32p), i32p], ctypes.c_int)
+    sig("pva_seg_desc_cu_seqlens", [vp, ctypes.POINTER(i32p), i32p], ctypes.c_int)
+    sig("pva_seg_desc_useful_flops", [vp], ctypes.c_int64)
+    sig("pva_seg_desc_tile", [vp, i32p, i32p], ctypes.c_int)
+    sig("pva_seg_desc_work_items", [vp, ctypes.POINTER(i32p), i32p], ctypes.c_int)
+    sig("pva_seg_desc_free", [vp], None)
+    sig("packed_attn_fwd", [vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_varlen", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_varlen_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("pva_last_error", [], ctypes.c_char_p)
+    sig("pva_version", [], ctypes.c_char_p)
     _lib_handle = L
     return L
 
@@ -408,6 +395,36 @@ def packed_attn_fwd_partial(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDe
                                        ctypes.c_void_p(_stream_handle(stream)))
     _check(st)
     return out_f32, lse
+
+
+def packed_attn_fwd_paged(q, k_pool, v_pool, block_table, cu_seqlens_q, seg_desc: SegDesc, scale: float, out,
+                          stream=None):
+    """bf16 forward with K/V in paged pools [num_blocks, block_size, H, D] and
+    a device int32 block table [nseq, stride]; q / out hold the queried rows."""
+    import torch
+    Nq, H, D = seg_desc.total_q, seg_desc.num_heads, seg_desc.head_dim
+    if (not isinstance(q, torch.Tensor) or not q.is_cuda or q.dtype != torch.bfloat16 or tuple(q.shape) != (Nq, H, D)
+            or not q.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"q must be a contiguous device bf16 [{Nq}, {H}, {D}] tensor")
+    for name, t in (("k_pool", k_pool), ("v_pool", v_pool)):
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 or t.dim() != 4
+                or tuple(t.shape[2:]) != (H, D) or not t.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a contiguous device bf16 [blocks, block_size, {H}, {D}]")
+    if k_pool.shape != v_pool.shape:
+        raise PvaError(PVA_ERR_INVALID_ARG, "k_pool and v_pool differ in shape")
+    if (not isinstance(block_table, torch.Tensor) or not block_table.is_cuda or block_table.dtype != torch.int32
+            or block_table.dim() != 2 or block_table.shape[0] != seg_desc.nseq or not block_table.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"block_table must be a contiguous device int32 [{seg_desc.nseq}, stride]")
+    if (not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.bfloat16
+            or tuple(out.shape) != (Nq, H, D) or not out.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out must be a contiguous device bf16 [{Nq}, {H}, {D}] tensor")
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    st = lib().packed_attn_fwd_paged(_ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table),
+                                     int(block_table.shape[1]), int(k_pool.shape[1]), int(k_pool.shape[0]),
+                                     _ptr(cu_seqlens_q), seg_desc.handle, ctypes.c_float(scale), _ptr(out),
+                                     ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out
 
 
 def merge_partials(o_parts, lse_parts, out, lse_out=None, stream=None):

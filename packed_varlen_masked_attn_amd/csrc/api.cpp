@@ -2,6 +2,7 @@
 // descriptor lifetime, error reporting and kernel dispatch.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -14,7 +15,7 @@
 
 namespace pva {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, int out_f32, float* lse, hipStream_t stream);
+                    float scale, void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream);
 int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int64_t rows, int head_dim, void* out,
                  float* lse_out, hipStream_t stream);
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks,
@@ -154,7 +155,7 @@ int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, c
   if (st != PVA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, out_f32, lse, s);
+  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, out_f32, lse, nullptr, s);
   if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
   return ok();
 }
@@ -292,6 +293,45 @@ int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const i
   if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out_f32, 1, lse, stream);
+}
+
+int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
+                          int32_t table_stride, int32_t block_size, int32_t num_blocks, const int32_t* cu_seqlens_q,
+                          const pva_seg_desc* seg_desc, float scale, void* out, void* stream) {
+  // host checks first (the K/V pointers stand in for cu_seqlens_k, which paged K/V does not use)
+  int st = validate_fwd(q, k_pool, v_pool, cu_seqlens_q, cu_seqlens_q, seg_desc, scale, out, PVA_BF16);
+  if (st != PVA_OK) return st;
+  if (!block_table) return set_error(PVA_ERR_INVALID_ARG, "block_table is NULL");
+  if (seg_desc->plan.chunked()) return set_error(PVA_ERR_INVALID_ARG, "paged K/V takes whole-sequence descriptors");
+  if (block_size < pva::kBf16BlockN || (block_size & (block_size - 1)) != 0 || block_size > (1 << 20))
+    return set_error(PVA_ERR_INVALID_ARG, "block_size must be a power of two, >= 32 and <= 2^20");
+  if (num_blocks < 1) return set_error(PVA_ERR_INVALID_ARG, "num_blocks must be >= 1");
+  if (int64_t(num_blocks) * block_size * seg_desc->plan.num_heads * seg_desc->plan.head_dim > (int64_t(1) << 62))
+    return set_error(PVA_ERR_INVALID_ARG, "pool too large");
+  int64_t need = 0;
+  for (int32_t L : seg_desc->plan.seq_len) need = std::max<int64_t>(need, (int64_t(L) + block_size - 1) / block_size);
+  if (table_stride < need)
+    return set_error(PVA_ERR_INVALID_ARG, "table_stride is smaller than the blocks the longest sequence needs");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const char* env = std::getenv("PVA_CHECK");
+  if (env && std::strcmp(env, "1") == 0) {
+    if ((st = check_one_cu(cu_seqlens_q, seg_desc->plan.cu_seqlens_q, "cu_seqlens_q", s)) != PVA_OK) return st;
+    std::vector<int32_t> tbl(size_t(seg_desc->plan.nseq) * table_stride);
+    hipError_t e = hipMemcpyAsync(tbl.data(), block_table, tbl.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_error(e, "PVA_CHECK: reading block_table");
+    for (int32_t q = 0; q < seg_desc->plan.nseq; ++q) {
+      const int64_t nb = (int64_t(seg_desc->plan.seq_len[q]) + block_size - 1) / block_size;
+      for (int64_t b = 0; b < nb; ++b) {
+        const int32_t x = tbl[size_t(q) * table_stride + b];
+        if (x < 0 || x >= num_blocks) return set_error(PVA_ERR_INVALID_ARG, "PVA_CHECK: block_table entry out of range");
+      }
+    }
+  }
+  const pva::PagedKV pg{block_table, table_stride, block_size, num_blocks};
+  st = pva::launch_fwd_bf16(q, k_pool, v_pool, cu_seqlens_q, seg_desc, scale, out, 0, nullptr, &pg, s);
+  if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
+  return ok();
 }
 
 int pva_merge_partials(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,

@@ -248,15 +248,27 @@ struct Kernel {
   }
 };
 
-template <int D>
-__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf16* __restrict__ Q,
+// K / V in a paged pool [num_blocks, block_size, H, D]: key row r of
+// sequence s sits in pool block table[s * stride + r / block_size], row
+// r % block_size. block_size is a power of two and a multiple of the key
+// tile, so every tile lies inside one block.
+struct Paging {
+  const int32_t* table;
+  int32_t stride;       // table entries per sequence
+  int32_t block_shift;  // log2(block_size)
+  int32_t num_blocks;
+};
+
+template <int D, bool PAGED>
+__device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
                                                                     const __bf16* __restrict__ K,
                                                                     const __bf16* __restrict__ V,
                                                                     const int32_t* __restrict__ cu,
                                                                     const int32_t* __restrict__ lims,
                                                                     const WorkItem* __restrict__ items, int H,
                                                                     float scale_log2, void* __restrict__ O,
-                                                                    int out_f32, float* __restrict__ lse) {
+                                                                    int out_f32, float* __restrict__ lse,
+                                                                    Paging pg) {
   using Kn = Kernel<D>;
   using Cfg = typename Kn::Cfg;
   using s16x8 = typename Kn::s16x8;
@@ -282,13 +294,12 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   const uint32_t rs2 = uint32_t(rs) * 2u;  // bytes (the planner keeps L * rs2 below 2^31)
   // bytes from a head's first row of the sequence to the end of its last row
   const uint32_t head_bytes = uint32_t(L - 1) * rs2 + 2u * D;
-  const int32_t kseq = cu[it.seq];  // first K/V token of the sequence
+  constexpr bool paged = PAGED;
+  const int32_t kseq = paged ? 0 : cu[it.seq];  // first K/V token of the sequence (contiguous K/V)
   const int64_t base = int64_t(kseq) * rs + int64_t(it.head) * D;
   // Q and O hold the queried rows only: row r of the sequence is row qo_row + r - q0
   const int64_t qbase = int64_t(it.qo_row - it.q0) * rs + int64_t(it.head) * D;
   const __bf16* Qh = Q + qbase;
-  const uint8_t* Kb = reinterpret_cast<const uint8_t*>(K + base);
-  const uint8_t* Vb = reinterpret_cast<const uint8_t*>(V + base);
 
   // this lane's query row and its key limit; rows past the tile see all L
   // keys held (their outputs are never stored). The limits are stored per
@@ -308,21 +319,53 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   typename Kn::VLoader vld;
   kld.init(rs2, lane, wave);
   vld.init(rs2, lane, wave);
-  auto ld_k = [&](int t, uint8_t* stage) {
-    const uint32_t o = uint32_t(t * BN) * rs2;
-    kld.load(make_rsrc(Kb + o, head_bytes - o), stage, wave);
+  // paged K/V: a tile's pool block comes from the table (a scalar load). The
+  // loop reads the blocks of the next iteration's tiles one iteration ahead,
+  // so the load has landed by the barrier that starts that iteration. An
+  // entry outside [0, num_blocks) is clamped so that no load leaves the pool.
+  // (read through the constant address space: a scalar load, whose wait does
+  // not also wait for the K/V DMA the way a vector load's would)
+  typedef const __attribute__((address_space(4))) int32_t* const_i32p;
+  const const_i32p tbl = paged ? (const_i32p)(pg.table + int64_t(it.seq) * pg.stride) : nullptr;
+  // raw table entry of tile t's block; clamped where it is used, so that the
+  // scalar load is only waited for there
+  auto block_of = [&](int t) -> int {
+    if (!paged || t >= kend) return 0;
+    return tbl[(t * BN) >> pg.block_shift];
   };
-  auto ld_v = [&](int t, uint8_t* stage) {
-    const uint32_t o = uint32_t(t * BN) * rs2;
-    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, wave);
+  auto tile_src = [&](const __bf16* contiguous, int t, int blk, uint32_t& bytes) -> const uint8_t* {
+    const int k0 = t * BN;
+    if (paged) {
+      blk = min(max(blk, 0), pg.num_blocks - 1);
+      const int row = k0 & ((1 << pg.block_shift) - 1);
+      bytes = uint32_t(min(BN, L - k0) - 1) * rs2 + 2u * D;  // rows of the sequence in this tile
+      return reinterpret_cast<const uint8_t*>(contiguous + ((int64_t(blk) << pg.block_shift) + row) * rs +
+                                              int64_t(it.head) * D);
+    } else {
+      const uint32_t o = uint32_t(k0) * rs2;
+      bytes = head_bytes - o;
+      return reinterpret_cast<const uint8_t*>(contiguous + base) + o;
+    }
   };
-  if (kend > 0) ld_k(0, kst[0]);
-  if (kend > 1) ld_k(1, kst[1]);
-  if (kend > 0) ld_v(0, vst[0]);
-  if (kend > 2) ld_k(2, kst[2]);
-  if (kend > 1) ld_v(1, vst[1]);
-  if (kend > 3) ld_k(3, kst[3]);
-  if (kend > 2) ld_v(2, vst[2]);
+  auto ld_k = [&](int t, uint8_t* stage, int blk) {
+    uint32_t bytes;
+    const uint8_t* src = tile_src(K, t, blk, bytes);
+    kld.load(make_rsrc(src, bytes), stage, wave);
+  };
+  auto ld_v = [&](int t, uint8_t* stage, int blk) {
+    uint32_t bytes;
+    const uint8_t* src = tile_src(V, t, blk, bytes);
+    vld.load(make_rsrc(src, bytes), stage, wave);
+  };
+  if (kend > 0) ld_k(0, kst[0], block_of(0));
+  if (kend > 1) ld_k(1, kst[1], block_of(1));
+  if (kend > 0) ld_v(0, vst[0], block_of(0));
+  if (kend > 2) ld_k(2, kst[2], block_of(2));
+  if (kend > 1) ld_v(1, vst[1], block_of(1));
+  if (kend > 3) ld_k(3, kst[3], block_of(3));
+  if (kend > 2) ld_v(2, vst[2], block_of(2));
+  // pool blocks of the tiles the first loop iteration loads
+  int kblk = block_of(NS), vblk = block_of(NS - 1);
 
   // Q^T operands: chunk c holds d = 16c + 8g .. +7 of this lane's query row
   bf16x8 qf[NKC];
@@ -369,8 +412,12 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
     constexpr int SJ = decltype(sj_tag)::value;
     lds_barrier();  // every wave is done with S(j) (K stage SJ) and PV(j-1) (V stage SJ-1)
     const bool steady = j + NS < kend;
-    if (steady) ld_k(j + NS, kst[SJ]);
-    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
+    if (steady) ld_k(j + NS, kst[SJ], kblk);
+    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS], vblk);
+    if constexpr (PAGED) {  // the next iteration's blocks, read ahead
+      kblk = block_of(j + NS + 1);
+      vblk = block_of(j + NS);
+    }
     const int k1 = (j + 1) * BN;
     s16x8 va[Kn::NSTEP];  // V^T operands of PV(j), read during phase 1
     float e[16];
@@ -454,26 +501,54 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(const __bf1
   }
 }
 
+// Two kernels over the same body: K/V contiguous in [N, H, D], or paged.
+template <int D>
+__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
+    float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse) {
+  fwd_bf16_body<D, false>(Q, K, V, cu, lims, items, H, scale_log2, O, out_f32, lse, Paging{nullptr, 0, 0, 0});
+}
+
+template <int D>
+__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_paged_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
+    float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse, Paging pg) {
+  fwd_bf16_body<D, true>(Q, K, V, cu, lims, items, H, scale_log2, O, out_f32, lse, pg);
+}
+
 template <int D>
 int launch(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d, float scale,
-           void* out, int out_f32, float* lse, hipStream_t stream) {
+           void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream) {
   using Cfg = Bf16Cfg<D>;
   const int n = static_cast<int>(d->plan.items.size());
   if (n == 0) return PVA_OK;
   const float scale_log2 = static_cast<float>(double(scale) * 1.4426950408889634);
-  hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, static_cast<const __bf16*>(q),
-                     static_cast<const __bf16*>(k), static_cast<const __bf16*>(v), cu, d->d_lims,
-                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2, out, out_f32, lse);
+  const auto* qp = static_cast<const __bf16*>(q);
+  const auto* kp = static_cast<const __bf16*>(k);
+  const auto* vp = static_cast<const __bf16*>(v);
+  const auto* items = static_cast<const WorkItem*>(d->d_items);
+  if (paged) {
+    int shift = 0;
+    while ((1 << shift) < paged->block_size) ++shift;
+    const Paging pg{paged->table, paged->stride, shift, paged->num_blocks};
+    hipLaunchKernelGGL(fwd_bf16_paged_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, qp, kp, vp, cu, d->d_lims, items,
+                       d->plan.num_heads, scale_log2, out, out_f32, lse, pg);
+  } else {
+    hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, qp, kp, vp, cu, d->d_lims, items,
+                       d->plan.num_heads, scale_log2, out, out_f32, lse);
+  }
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;
 }
 
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, int out_f32, float* lse, hipStream_t stream) {
+                    float scale, void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream) {
   switch (d->plan.head_dim) {
-    case 64: return launch<64>(q, k, v, cu, d, scale, out, out_f32, lse, stream);
-    case 128: return launch<128>(q, k, v, cu, d, scale, out, out_f32, lse, stream);
+    case 64: return launch<64>(q, k, v, cu, d, scale, out, out_f32, lse, paged, stream);
+    case 128: return launch<128>(q, k, v, cu, d, scale, out, out_f32, lse, paged, stream);
     default: return PVA_ERR_UNSUPPORTED;
   }
 }

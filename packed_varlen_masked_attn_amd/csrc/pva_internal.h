@@ -73,6 +73,14 @@ struct Plan {
   }
 };
 
+// K / V held in a paged pool [num_blocks, block_size, H, D] (device table).
+struct PagedKV {
+  const int32_t* table;  // device int32 [nseq * stride]: pool block of each block of keys
+  int32_t stride;        // table entries per sequence
+  int32_t block_size;    // keys per block: a power of two, a multiple of the key tile
+  int32_t num_blocks;    // blocks in each pool
+};
+
 // Validates and plans; on failure returns a status and fills `err`.
 // Two segments per sequence: text (causal) then one image block (full).
 int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,

@@ -212,3 +212,31 @@ def test_partial_and_merge_reject_on_host():
     # a chunked descriptor cannot go through the whole-sequence entry point
     d2 = pva.SegDesc.segments([([8, 8], [0, 1])], 2, 64, host_only=True, k_lo=[4], k_hi=[8])
     assert L.packed_attn_fwd(p, p, p, p, d2.handle, ctypes.c_float(0.1), p, None) == pva.PVA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("case", ["null_table", "block_not_pow2", "block_too_small", "no_blocks", "short_stride",
+                                  "chunked", "fp8_desc", "host_only"])
+def test_paged_rejects_on_host(case):
+    L = pva.lib()
+    p = ctypes.c_void_p(FAKE)
+    seqs = [([40, 300], [0, 1], 40), ([10, 20], [0, 1], 0)]
+    desc = pva.SegDesc.segments(seqs, 2, 64, host_only=True)
+    table, stride, bs, nb = p, 12, 32, 50
+    if case == "null_table":
+        table = None
+    elif case == "block_not_pow2":
+        bs = 96
+    elif case == "block_too_small":
+        bs = 16
+    elif case == "no_blocks":
+        nb = 0
+    elif case == "short_stride":
+        stride = 10  # the 340-token sequence needs 11 blocks of 32
+    elif case == "chunked":
+        desc = pva.SegDesc.segments(seqs, 2, 64, host_only=True, k_lo=[0, 0], k_hi=[100, 30])
+    elif case == "fp8_desc":
+        desc = pva.SegDesc.segments(seqs, 2, 128, "fp8", host_only=True)
+    st = L.packed_attn_fwd_paged(p, p, p, table, stride, bs, nb, p, desc.handle, ctypes.c_float(0.1), p, None)
+    assert st == pva.PVA_ERR_INVALID_ARG
+    if case == "host_only":
+        assert "host-only" in L.pva_last_error().decode()
