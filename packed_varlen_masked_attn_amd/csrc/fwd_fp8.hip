@@ -12,7 +12,7 @@
 //
 // Per wave and key tile j:
 //   S^T[key, q] = K Q^T     two 32-key blocks x two 64-wide steps over d;
-//                           A = K from LDS (32 contiguous bytes per lane),
+//                           A = K from LDS (two 16-byte reads per lane),
 //                           B = Q^T in registers for the whole item.
 //   softmax in fp32, log2 domain, with the score scale q_s * k_s * scale
 //   folded into the exponent; lazy rescaling as in the bf16 kernel.
@@ -48,11 +48,23 @@ struct Fp8Cfg {
   static constexpr int NKS = D / 64;   // 64-wide MFMA steps over d for S^T
   static constexpr int NDB = D / 32;   // 32-row blocks of O^T (plus one block for l)
   static constexpr int NS = 4;         // LDS stages per tensor
-  // K rows padded by one chunk (conflict-free 16-byte operand reads, affine
-  // addresses); V rows unpadded with XOR-swizzled 32-byte pairs
-  static constexpr int KROW = C + 1, KSLOTS = BN * KROW, KTILE = KSLOTS * 16;
+  // K and V rows unpadded (C 16-byte chunks each). K's chunks are
+  // XOR-permuted per row: the 16-byte operand reads of 16 consecutive rows
+  // at one logical chunk then touch 16 different 16-byte bank groups (rows
+  // of one parity share 8 groups, which the permutation (r / 2) mod 8
+  // spreads). V's 32-byte column pairs are XOR-swizzled for the transpose
+  // reads (vswz below).
+  static constexpr int KROW = C, KSLOTS = BN * KROW, KTILE = KSLOTS * 16;
   static constexpr int VROW = C, VSLOTS = BN * VROW, VTILE = VSLOTS * 16;
+  static_assert(C == 8, "the K permutation is written for 8 chunks per row");
+  static __device__ __forceinline__ int kswz(int r) { return (r >> 1) & (C - 1); }
+  // every wave issues exactly this many DMA instructions per tile
   static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
+  static_assert(KSLOTS % NT == 0 && VSLOTS % NT == 0, "uniform DMA rounds");
+};
+
+struct KSwizzledChunks {
+  static __device__ __forceinline__ int chunk(int row, int pos) { return pos ^ Fp8Cfg::kswz(row); }
 };
 
 // Position of a V row's 32-byte column pairs: pair p of row k sits at pair
@@ -76,13 +88,27 @@ __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const
 struct Fp8Kernel {
   using Cfg = Fp8Cfg;
   static constexpr int BN = Cfg::BN, NB = Cfg::NB, C = Cfg::C, NKS = Cfg::NKS, NDB = Cfg::NDB;
-  using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, PaddedRows<C>>;
+  using KLoader = BufLoader<Cfg::NT, Cfg::KROW, Cfg::KSLOTS, KSwizzledChunks>;
   using VLoader = BufLoader<Cfg::NT, Cfg::VROW, Cfg::VSLOTS, VSwizzledPairs>;
 
   // K operand of 64-wide step c for key block b: row 32 b + l32, bytes
-  // 64 c + 32 g .. +31 (any d assignment works as long as Q uses the same)
-  static __device__ __forceinline__ i32x8 read_k(const uint8_t* kst, int b, int c, int l32, int g) {
-    return *reinterpret_cast<const i32x8*>(kst + 16 * Cfg::KROW * (32 * b + l32) + 64 * c + 32 * g);
+  // 64 c + 32 g .. +31, i.e. logical chunks 4 c + 2 g and 4 c + 2 g + 1 (any
+  // d assignment works as long as Q uses the same). The permutation depends
+  // on the row only through (l32 / 2) mod 8, so block b adds an immediate.
+  struct KAddr {
+    uint32_t o[NKS][2];
+    __device__ __forceinline__ void init(int l32, int g) {
+      const int sw = Cfg::kswz(l32);
+#pragma unroll
+      for (int c = 0; c < NKS; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) o[c][h] = uint32_t(16 * C * l32 + 16 * ((4 * c + 2 * g + h) ^ sw));
+    }
+  };
+  static __device__ __forceinline__ i32x8 read_k(const uint8_t* kst, int b, int c, const KAddr& ka) {
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(kst + 16 * C * 32 * b + ka.o[c][0]);
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(kst + 16 * C * 32 * b + ka.o[c][1]);
+    return i32x8(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
   }
 
   // V^T operand of column block db: byte 8 r + e of lane l is
@@ -132,17 +158,17 @@ struct Fp8Kernel {
   // the probabilities of tile j (program-order interleave, bounded registers)
   static __device__ __forceinline__ void s_with_probs(f32x16 (&snext)[NB], const uint8_t* kst,
                                                       const i32x8 (&qf)[NKS], const f32x16 (&scur)[NB],
-                                                      float scale_log2, float m, i32x8& pb, int l32, int g) {
+                                                      float scale_log2, float m, i32x8& pb, const KAddr& kad) {
     constexpr int NSTEP = NB * NKS;  // (b, c) pairs
     constexpr int WPS = 8 / NSTEP;   // packed probability dwords per MFMA step
-    i32x8 ka = read_k(kst, 0, 0, l32, g);
+    i32x8 ka = read_k(kst, 0, 0, kad);
 #pragma unroll
     for (int b = 0; b < NB; ++b) snext[b] = f32x16{};
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       const int c = st / NB, b = st % NB;
       i32x8 kn;
-      if (st + 1 < NSTEP) kn = read_k(kst, (st + 1) % NB, (st + 1) / NB, l32, g);
+      if (st + 1 < NSTEP) kn = read_k(kst, (st + 1) % NB, (st + 1) / NB, kad);
       snext[b] = mfma_fp8(ka, qf[c], snext[b]);
 #pragma unroll
       for (int ww = 0; ww < WPS; ++ww) {
@@ -314,6 +340,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const int vrow0[1] = {8 * (e >> 2) + 4 * g + (e & 3)};
   const int vsw = vswz(vrow0[0]);
   const int half = (lane >> 4) & 1, p8 = 8 * (lane & 1);
+  typename Kn::KAddr kad;
+  kad.init(l32, g);
 
   if (kend > 3)
     wait_vmcnt<2 * Cfg::DMA_MIN>();
@@ -327,7 +355,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
 #pragma unroll
     for (int c = 0; c < NKS; ++c)
 #pragma unroll
-      for (int b = 0; b < NB; ++b) s[b] = mfma_fp8(Kn::read_k(kt, b, c, l32, g), qf[c], s[b]);
+      for (int b = 0; b < NB; ++b) s[b] = mfma_fp8(Kn::read_k(kt, b, c, kad), qf[c], s[b]);
   };
 
   f32x16 sa[NB], sb[NB];
@@ -348,7 +376,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     const int k1 = (j + 1) * BN;
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
-    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run, pb, l32, g);
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run, pb, kad);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
     const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, scale_log2, vrow0, vsw, half, p8);

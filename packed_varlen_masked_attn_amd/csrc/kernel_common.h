@@ -102,11 +102,4 @@ struct BufLoader {
   }
 };
 
-// Row-padded layout: the first CHUNKS slots of a row are the row's chunks in
-// order, the rest are pad.
-template <int CHUNKS>
-struct PaddedRows {
-  static __device__ __forceinline__ int chunk(int, int pos) { return pos < CHUNKS ? pos : -1; }
-};
-
 }  // namespace pva
