@@ -187,6 +187,13 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
     load[x] += g.cost;
     bins[x].insert(bins[x].end(), g.items.begin(), g.items.end());
   }
+  // Each XCD's queue runs longest item first. The dispatcher hands out
+  // workgroups in index order, round-robin over the XCDs, and waits when the
+  // next one's XCD has no free slot; with the queues in cost order the items
+  // at one position finish at about the same time on every XCD, which keeps
+  // those waits short (stable: a group's items stay together).
+  for (auto& b : bins)
+    std::stable_sort(b.begin(), b.end(), [&](const WorkItem& u, const WorkItem& v) { return item_cost(u) > item_cost(v); });
   // Workgroups are dispatched to XCDs round-robin by workgroup index, so slot
   // j of XCD x sits at list position j * kNumXcd + x; shorter bins are padded
   // with empty slots to keep that alignment.
