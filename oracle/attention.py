@@ -37,19 +37,20 @@ def offsets(seq_len: Sequence[int]) -> np.ndarray:
     return out
 
 
-def mixed_mask(text_len: int, seq_len: int) -> np.ndarray:
+def mixed_mask(text_len: int, seq_len: int, rows: Optional[Iterable[int]] = None) -> np.ndarray:
     """Boolean [L, L]: True where query row i may attend to key j.
 
     Rows below ``text_len`` are causal over the text prefix (j <= i); every
-    later row (an image token) sees all L keys.
+    later row (an image token) sees all L keys. With ``rows``, only those
+    rows ([len(rows), L]), so that long sequences need no L x L array.
     """
     L, T = int(seq_len), int(text_len)
     if T < 0 or T > L:
         raise ValueError("text_len must lie in [0, seq_len]")
-    i = np.arange(L)[:, None]
+    i = (np.arange(L) if rows is None else np.asarray(list(rows), dtype=np.int64))[:, None]
     j = np.arange(L)[None, :]
     causal = j <= i
-    is_image_row = np.broadcast_to(i >= T, (L, L))
+    is_image_row = np.broadcast_to(i >= T, (i.shape[0], L))
     return np.where(is_image_row, True, causal)
 
 
@@ -123,8 +124,7 @@ def packed_attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray,
     a, L, T = int(off[seq]), seq_len[seq], int(text_len[seq])
     rows = np.asarray(list(rows), dtype=np.int64)
     heads = list(heads)
-    full = mixed_mask(T, L)
-    mask = full[rows]
+    mask = mixed_mask(T, L, rows)
     out = np.zeros((len(rows), len(heads), q.shape[2]), dtype=np.float64)
     for hi, h in enumerate(heads):
         qs = np.asarray(q[a + rows, h], dtype=np.float64)

@@ -67,6 +67,7 @@ def _build_host(t, i, H=2, D=128, dtype=0):
     ([2 ** 24 - 1] * 129, [0] * 129, 1, 64, 0, pva.PVA_ERR_INVALID_ARG),  # N overflows int32
     ([2 ** 24], [0], 1, 64, 0, pva.PVA_ERR_UNSUPPORTED),      # L * H * D * 2 = 2^31
     ([100], [2 ** 20], 16, 64, 0, pva.PVA_ERR_UNSUPPORTED),   # L * H * D * 2 > 2^31
+    ([1000], [64536], 128, 128, 0, pva.PVA_ERR_UNSUPPORTED),  # L = 65,536 at H = D = 128: exactly 2^31
 ])
 def test_build_rejects(t, i, H, D, dtype, code):
     if t:

@@ -239,6 +239,13 @@ def test_rows_helper_matches_full():
         assert np.array_equal(part, full[off[s] + np.array(rows)][:, [0, 2]])
 
 
+def test_mask_rows_match_full_mask():
+    rng = np.random.default_rng(12)
+    for T, L in [(0, 9), (9, 9), (3, 17), (16, 40), (1, 1)]:
+        rows = sorted(set(int(x) for x in rng.integers(0, L, 7)) | {0, L - 1, min(T, L - 1)})
+        assert np.array_equal(oracle.mixed_mask(T, L, rows), oracle.mixed_mask(T, L)[rows])
+
+
 # ---------------------------------------------------------------- useful FLOPs
 
 def test_useful_flops_by_counting_mask():

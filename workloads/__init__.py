@@ -239,6 +239,23 @@ def bf16_inputs(w: Workload):
     return to_bf16(q), to_bf16(k), to_bf16(v)
 
 
+def device_normal_bf16(w: Workload, device):
+    """Q, K, V as device bf16 [N, H, D]: standard normals from torch's seeded
+    device generator (Philox, seed ``w.seed``), drawn in q, k, v order in
+    float32 and cast with round-to-nearest-even. For shapes whose host draw
+    would take minutes (a billion elements per tensor); the oracle reads the
+    heads and rows it checks back from these tensors."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(int(w.seed))
+    shape = (w.total_tokens, w.num_heads, w.head_dim)
+    out = []
+    for _ in range(3):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        out.append(x.to(torch.bfloat16))
+        del x
+    return tuple(out)
+
+
 def seq_bounds(w: Workload) -> List[Tuple[int, int]]:
     """(start, end) token range of each sequence in pack order."""
     out, a = [], 0
