@@ -85,7 +85,8 @@ typedef struct pva_seg_desc pva_seg_desc;
  *   nseq                : >= 1, sum of lengths must fit in int32
  *   num_heads           : H >= 1, H * head_dim * N must fit in int64
  *   head_dim            : D in {64, 128}
- *                         (every sequence needs L * H * D * 2 < 2^31: one head's
+ *                         (every sequence needs L * H * D * e < 2^31, e = 2
+ *                         bytes per bf16 element, 1 per fp8 code: one head's
  *                         rows are addressed with 32-bit byte offsets;
  *                         PVA_ERR_UNSUPPORTED otherwise)
  *   dtype               : element type of Q/K/V the descriptor will serve

@@ -77,6 +77,7 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
   p.num_heads = num_heads;
   p.head_dim = head_dim;
   p.tile = tile_shape(dtype, head_dim);
+  const int64_t esize = dtype == PVA_FP8_E4M3 ? 1 : 2;  // bytes per Q/K/V element
   p.seq_len.resize(nseq);
   p.q_start.resize(nseq);
   p.k_lo.resize(nseq);
@@ -95,9 +96,10 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
     if (lo < 0 || lo > hi || hi > L) return fail(err, PVA_ERR_INVALID_ARG, "key chunk must satisfy 0 <= k_lo <= k_hi <= L");
     const int64_t Lk = hi - lo;
     // the kernels address one head's rows of a sequence with 32-bit byte
-    // offsets below 2^31 (row stride H * D elements of at most 2 bytes)
-    if (Lk * int64_t(num_heads) * head_dim * 2 >= (int64_t(1) << 31))
-      return fail(err, PVA_ERR_UNSUPPORTED, "sequence too long for 32-bit head addressing (L * H * D * 2 >= 2^31)");
+    // offsets below 2^31 (row stride H * D elements of `esize` bytes)
+    if (Lk * int64_t(num_heads) * head_dim * esize >= (int64_t(1) << 31))
+      return fail(err, PVA_ERR_UNSUPPORTED,
+                  "sequence too long for 32-bit head addressing (L * H * D * element bytes >= 2^31)");
     total += Lk;
     total_q += L - qs;
     if (total > INT32_MAX || total_q > INT32_MAX)

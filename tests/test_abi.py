@@ -55,6 +55,14 @@ def _build_host(t, i, H=2, D=128, dtype=0):
     return st, h
 
 
+def test_build_accepts_largest_slices():
+    # the longest sequences at H = D = 128: L * H * D * e = 2^31 - 2^15 (bf16) or - 2^14 (fp8)
+    for L, dtype in ((65535, 0), (131071, 1)):
+        st, h = _build_host([1000], [L - 1000], 128, 128, dtype)
+        assert st == pva.PVA_OK, pva.lib().pva_last_error()
+        pva.lib().pva_seg_desc_free(h)
+
+
 @pytest.mark.parametrize("t,i,H,D,dtype,code", [
     ([], [], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),             # nseq = 0
     ([-1], [4], 2, 128, 0, pva.PVA_ERR_INVALID_ARG),          # T < 0
@@ -68,6 +76,7 @@ def _build_host(t, i, H=2, D=128, dtype=0):
     ([2 ** 24], [0], 1, 64, 0, pva.PVA_ERR_UNSUPPORTED),      # L * H * D * 2 = 2^31
     ([100], [2 ** 20], 16, 64, 0, pva.PVA_ERR_UNSUPPORTED),   # L * H * D * 2 > 2^31
     ([1000], [64536], 128, 128, 0, pva.PVA_ERR_UNSUPPORTED),  # L = 65,536 at H = D = 128: exactly 2^31
+    ([1000], [130072], 128, 128, 1, pva.PVA_ERR_UNSUPPORTED),  # fp8 (1 byte): L = 131,072 -> exactly 2^31
 ])
 def test_build_rejects(t, i, H, D, dtype, code):
     if t:

@@ -304,6 +304,33 @@ def fp8_inputs(w: Workload):
     return q8, k8, v8, qs, ks, vs
 
 
+def device_fp8_inputs(w: Workload, device):
+    """(q8, k8, v8, q_scale, k_scale, v_scale) on the device: the draws of
+    ``device_normal_bf16`` (before the bf16 cast) quantised per (sequence,
+    head) as ``quantize_e4m3_rows`` does (absmax / 448, saturating round to
+    nearest even); codes as uint8 [N, H, D], scales float32 [nseq, H]."""
+    import torch
+    g = torch.Generator(device=device).manual_seed(int(w.seed))
+    shape = (w.total_tokens, w.num_heads, w.head_dim)
+    out, scales = [], []
+    for _ in range(3):
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        codes = torch.empty(shape, dtype=torch.uint8, device=device)
+        sc = torch.ones((w.nseq, w.num_heads), dtype=torch.float32, device=device)
+        a = 0
+        for s, n in enumerate(w.seq_len):
+            if n > 0:
+                amax = x[a:a + n].abs().amax(dim=(0, 2))
+                sc[s] = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+                q = torch.clamp(x[a:a + n] / sc[s][None, :, None], -E4M3_MAX, E4M3_MAX)
+                codes[a:a + n] = q.to(torch.float8_e4m3fn).view(torch.uint8)
+            a += n
+        del x
+        out.append(codes)
+        scales.append(sc)
+    return out[0], out[1], out[2], scales[0], scales[1], scales[2]
+
+
 def random_lengths(rng: np.random.Generator, nreq: int, tmax: int, imax: int,
                    allow_empty_text: bool = True, allow_empty_image: bool = True) -> Tuple[Tuple[int, ...], Tuple[int, ...]]:
     """Random CFG-paired (text_len, image_len) lists with every sequence non-empty."""
