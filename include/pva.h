@@ -257,6 +257,18 @@ int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const i
                             float* out_f32, float* lse, void* stream);
 
 /*
+ * FP8 variant of packed_attn_fwd_partial (scales as in packed_attn_fwd_fp8;
+ * the descriptor must have been built with dtype PVA_FP8_E4M3). The dot
+ * products are those of the dequantised inputs, q.k_j = q_s k_s (codes'
+ * product), and O and lse use the weights PV applied, i.e. the E4M3
+ * probabilities, so the chunks of one row merge exactly as in the bf16 case.
+ */
+int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                float* out_f32, float* lse, void* stream);
+
+/*
  * Forward with K and V in a paged pool (the scheduler-managed paged KV mode
  * of "HunyuanImage-3.0-Instruct DiT Image Generation on 4x GPU", section
  * "Scheduler-managed paged KV": unquantised bf16 K/V in a fixed physical

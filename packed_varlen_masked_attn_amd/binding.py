@@ -34,6 +34,7 @@ EXPORTED = [
     "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
     "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
     "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials", "packed_attn_fwd_paged",
+    "packed_attn_fwd_partial_fp8",
 ]
 
 
@@ -76,6 +77,7 @@ def lib() -> ctypes.CDLL:
     sig("pva_seg_desc_build_kv_chunk_host", [i32p, i32p, i32p, i32p, i32p, i32p, ctypes.c_int32,
                                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
     sig("packed_attn_fwd_partial", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_partial_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp], ctypes.c_int)
     sig("packed_attn_fwd_paged", [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                         ctypes.c_float, vp, vp], ctypes.c_int)
     sig("pva_merge_partials", [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp], ctypes.c_int)
@@ -393,6 +395,40 @@ def packed_attn_fwd_partial(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDe
     st = lib().packed_attn_fwd_partial(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
                                        seg_desc.handle, ctypes.c_float(scale), _ptr(out_f32), _ptr(lse),
                                        ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out_f32, lse
+
+
+def _check_partial_out(desc: SegDesc, out_f32, lse) -> None:
+    import torch
+    Nq, H, D = desc.total_q, desc.num_heads, desc.head_dim
+    if (not isinstance(out_f32, torch.Tensor) or not out_f32.is_cuda or out_f32.dtype != torch.float32
+            or tuple(out_f32.shape) != (Nq, H, D) or not out_f32.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out_f32 must be a contiguous device float32 [{Nq}, {H}, {D}] tensor")
+    if (not isinstance(lse, torch.Tensor) or not lse.is_cuda or lse.dtype != torch.float32
+            or tuple(lse.shape) != (Nq, H) or not lse.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"lse must be a contiguous device float32 [{Nq}, {H}] tensor")
+
+
+def packed_attn_fwd_partial_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDesc,
+                                scale: float, out_f32, lse, stream=None):
+    """fp8 variant of packed_attn_fwd_partial: fp32 O ([total_q, H, D]) and the
+    rows' log-sum-exp ([total_q, H]); returns (out_f32, lse)."""
+    import torch
+    Nq, H, D = seg_desc.total_q, seg_desc.num_heads, seg_desc.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        N = Nq if name == "q" else seg_desc.total_tokens
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype not in (torch.float8_e4m3fn, torch.uint8)
+                or tuple(t.shape) != (N, H, D) or not t.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a contiguous device E4M3 [{N}, {H}, {D}] tensor")
+    _check_partial_out(seg_desc, out_f32, lse)
+    _check_scales(seg_desc, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_partial_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale),
+                                           _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), seg_desc.handle,
+                                           ctypes.c_float(scale), _ptr(out_f32), _ptr(lse),
+                                           ctypes.c_void_p(_stream_handle(stream)))
     _check(st)
     return out_f32, lse
 

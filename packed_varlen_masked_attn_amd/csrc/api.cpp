@@ -19,8 +19,8 @@ int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* 
 int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int64_t rows, int head_dim, void* out,
                  float* lse_out, hipStream_t stream);
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks,
-                   const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, void* out,
-                   hipStream_t stream);
+                   const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, void* out, int out_f32,
+                   float* lse, hipStream_t stream);
 }  // namespace pva
 
 namespace {
@@ -162,13 +162,13 @@ int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, c
 
 int fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
             const float* v_scale, const int32_t* cu_q, const int32_t* cu_k, const pva_seg_desc* d, float scale,
-            void* out, void* stream) {
+            void* out, int out_f32, float* lse, void* stream) {
   int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_FP8_E4M3);
   if (st != PVA_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, s);
+  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, out_f32, lse, s);
   if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
   if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
   return ok();
@@ -354,14 +354,26 @@ int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float
                         void* out, void* stream) {
   int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, cu_seqlens, seg_desc, scale, out, stream);
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, cu_seqlens, seg_desc, scale, out, 0, nullptr,
+                 stream);
 }
 
 int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                                const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
                                void* stream) {
-  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, stream);
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, 0, nullptr,
+                 stream);
+}
+
+int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                float* out_f32, float* lse, void* stream) {
+  if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
+  if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out_f32, 1, lse,
+                 stream);
 }
 
 const char* pva_last_error(void) { return g_last_error.c_str(); }

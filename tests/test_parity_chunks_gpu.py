@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, err_stats, f64, say
+from gpu_util import BF16_MAX_ABS, BF16_MEAN_ABS, FP8_MAX_ABS, err_stats, f64, say
 
 pytestmark = pytest.mark.gpu
 
@@ -178,3 +178,98 @@ def test_full_size_two_chunks_merged_sampled():
         mx, mean = err_stats(got, ref)
         say(f"[chunks] full size seq {si}: max {mx:.3e} mean {mean:.3e}")
         assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
+
+
+# ---------------------------------------------------------------- fp8 partials
+
+# l is the sum of the E4M3 weights PV applied (RNE, relative error <= 2^-4
+# each), so |lse - oracle| <= ln(1 + 2^-4) < 6.1e-2 at worst
+FP8_LSE_MAX_ABS = 6.1e-2
+
+
+def _fp8_case(seqs, H, D, seed):
+    """E4M3 codes and scales (per sequence and head, over the queried rows for
+    Q, over the whole sequence for K and V) plus their fp64 dequantisation."""
+    import torch
+    from oracle import fp8 as ofp8
+    sw = workloads.SegWorkload("chunks_fp8", tuple((tuple(s.seg_len), tuple(s.seg_kind), s.q_start) for s in seqs),
+                               H, D, seed, "fp8")
+    q8, k8, v8, qs, ks, vs = workloads.seg_fp8_inputs(sw)
+    codes = [x.view(torch.uint8) for x in (q8, k8, v8)]
+    deq = (ofp8.dequantize(codes[0].numpy(), qs, sw.q_rows), ofp8.dequantize(codes[1].numpy(), ks, sw.seq_len),
+           ofp8.dequantize(codes[2].numpy(), vs, sw.seq_len))
+    return codes, (qs, ks, vs), deq
+
+
+def _partial_fp8(seqs, codes, scales, lo, hi, H, D):
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    desc = pva.SegDesc.segments([(s.seg_len, s.seg_kind, s.q_start) for s in seqs], H, D, "fp8", k_lo=lo, k_hi=hi)
+    q = codes[0].to("cuda")
+    k = _chunk_rows(codes[1], seqs, lo, hi).to("cuda")
+    v = _chunk_rows(codes[2], seqs, lo, hi).to("cuda")
+    sc = [torch.from_numpy(x).to("cuda") for x in scales]
+    cuq = torch.from_numpy(desc.cu_seqlens_q).to("cuda")
+    cuk = torch.from_numpy(desc.cu_seqlens).to("cuda")
+    o = torch.empty((desc.total_q, H, D), dtype=torch.float32, device="cuda")
+    lse = torch.empty((desc.total_q, H), dtype=torch.float32, device="cuda")
+    pva.packed_attn_fwd_partial_fp8(q, k, v, *sc, cuq, cuk, desc, 1 / math.sqrt(D), o, lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_partial_fp8(o, lse, ref_o, ref_l):
+    got_l = lse.cpu().numpy().astype(np.float64)
+    inf = np.isneginf(ref_l)
+    assert np.array_equal(np.isneginf(got_l), inf), "rows without keys must give exactly -inf"
+    assert np.all(o.cpu().numpy()[inf] == 0.0), "rows without keys must give exactly zero"
+    lmax = float(np.max(np.abs(got_l[~inf] - ref_l[~inf]))) if (~inf).any() else 0.0
+    assert lmax <= FP8_LSE_MAX_ABS
+    mx, _ = err_stats(o.cpu().numpy().astype(np.float64), ref_o)
+    assert mx <= FP8_MAX_ABS, mx
+    return mx, lmax
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_partial_over_whole_sequences(seed):
+    rng = np.random.default_rng(2100 + seed)
+    seqs = _random_seqs(rng, 3)
+    H, D = 2, 128
+    codes, scales, (qn, kn, vn) = _fp8_case(seqs, H, D, 110 + seed)
+    lo, hi = [0] * len(seqs), [s.length for s in seqs]
+    o, lse = _partial_fp8(seqs, codes, scales, lo, hi, H, D)
+    ref_o, ref_l = oracle.chunk_attention(qn, kn, vn, seqs, lo, hi, 1 / math.sqrt(D))
+    mx, lmax = _check_partial_fp8(o, lse, ref_o, ref_l)
+    say(f"[chunks] fp8 whole seqs seed {seed}: O max {mx:.3e}, lse max {lmax:.3e}")
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_fp8_chunked_partials_and_merge(seed):
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    rng = np.random.default_rng(2200 + seed)
+    seqs = _random_seqs(rng, 3)
+    H, D = 2, 128
+    codes, scales, (qn, kn, vn) = _fp8_case(seqs, H, D, 120 + seed)
+    cuts = [sorted(int(x) for x in rng.integers(0, s.length + 1, 2)) for s in seqs]
+    bounds = [((0, c[0], c[1]), (c[0], c[1], s.length)) for c, s in zip(cuts, seqs)]
+    os_, ls_ = [], []
+    for p in range(3):
+        lo = [b[0][p] for b in bounds]
+        hi = [b[1][p] for b in bounds]
+        o, lse = _partial_fp8(seqs, codes, scales, lo, hi, H, D)
+        ref_o, ref_l = oracle.chunk_attention(qn, _chunk_rows(kn, seqs, lo, hi), _chunk_rows(vn, seqs, lo, hi),
+                                              seqs, lo, hi, 1 / math.sqrt(D))
+        _check_partial_fp8(o, lse, ref_o, ref_l)
+        os_.append(o)
+        ls_.append(lse)
+    out = torch.empty((sum(s.q_rows for s in seqs), H, D), dtype=torch.bfloat16, device="cuda")
+    lse_out = torch.empty((out.shape[0], H), dtype=torch.float32, device="cuda")
+    pva.merge_partials(torch.stack(os_), torch.stack(ls_), out, lse_out)
+    torch.cuda.synchronize()
+    full = oracle.segment_attention(qn, kn, vn, seqs, 1 / math.sqrt(D))
+    mx, mean = err_stats(f64(out), full)
+    say(f"[chunks] fp8 merged seed {seed}: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= FP8_MAX_ABS
+    _, full_l = oracle.chunk_attention(qn, kn, vn, seqs, [0] * len(seqs), [s.length for s in seqs], 1 / math.sqrt(D))
+    assert np.max(np.abs(lse_out.cpu().numpy() - full_l)) <= FP8_LSE_MAX_ABS
