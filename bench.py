@@ -236,7 +236,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     if args.split_keys > 1:
-        split_keys_bench(args, w, q, k, v, scale, flops, desc_us)
+        split_keys_bench(args, w, q, k, v, scale, flops, desc_us, (qsd, ksd, vsd) if is_fp8 else None)
         return
 
     if args.paged:
@@ -379,14 +379,16 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def split_keys_bench(args, w, q, k, v, scale, flops, desc_us):
+def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     """Ring attention's single-GPU half on the workload: each sequence's keys
     split into P equal chunks (their K/V copied apart beforehand, as a rank
-    would hold them), one partial launch per chunk, then one merge."""
+    would hold them), one partial launch per chunk, then one merge. fp8
+    workloads pass their (q, k, v) scales; K/V chunks keep their sequence's."""
     import torch
     import packed_varlen_masked_attn_amd as pva
-    if isinstance(w, workloads.SegWorkload) or w.dtype == "fp8":
-        sys.exit("--split-keys runs the two-segment bf16 workloads")
+    if isinstance(w, workloads.SegWorkload):
+        sys.exit("--split-keys runs the two-segment workloads")
+    dtype = "fp8" if fp8_scales is not None else "bf16"
     P, dev, H, D = args.split_keys, q.device, w.num_heads, w.head_dim
     seqs = [([t, i], [0, 1]) for t, i in zip(w.text_len, w.image_len)]
     off = np.cumsum([0] + list(w.seq_len))
@@ -394,7 +396,7 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us):
     for p in range(P):
         lo = [L * p // P for L in w.seq_len]
         hi = [L * (p + 1) // P for L in w.seq_len]
-        d = pva.SegDesc.segments(seqs, H, D, "bf16", k_lo=lo, k_hi=hi)
+        d = pva.SegDesc.segments(seqs, H, D, dtype, k_lo=lo, k_hi=hi)
         idx = torch.from_numpy(np.concatenate([np.arange(off[s] + a, off[s] + b) for s, (a, b) in
                                                enumerate(zip(lo, hi))]).astype(np.int64)).to(dev)
         parts.append((d, k.index_select(0, idx).contiguous(), v.index_select(0, idx).contiguous(),
@@ -408,7 +410,11 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us):
 
     def step(ev=None):
         for p, (d, kp, vp, cuk) in enumerate(parts):
-            pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, o_parts[p], l_parts[p], stream)
+            if fp8_scales is not None:
+                pva.packed_attn_fwd_partial_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, o_parts[p], l_parts[p],
+                                                stream)
+            else:
+                pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, o_parts[p], l_parts[p], stream)
         if ev is not None:
             ev.record(stream)
         pva.merge_partials(o_parts, l_parts, out, None, stream)
@@ -438,13 +444,14 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us):
         "metric": "useful attention TFLOP/s, key-split partials + merge (Ring attention's single-GPU half)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16", "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
+        "dtype": dtype, "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
         "config": {"workload": w.name, "split_keys": P, "text_len": list(w.text_len), "image_len": list(w.image_len),
                    "num_heads": H, "head_dim": D, "parallelism": "single GPU"},
         "partials_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5), "desc_build_us": round(desc_us, 1),
-        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["bf16"], 4), "traffic": None,
-                     "kernel": f"fwd_bf16_kernel<{D}> (all partial launches)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[dtype], 4), "traffic": None,
+                     "kernel": ("fwd_fp8_kernel" if dtype == "fp8" else f"fwd_bf16_kernel<{D}>") +
+                               " (all partial launches)"},
         "merge_roofline": {"bound": "hbm", "achieved": round(merge_bytes / merge_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
                            "unit": "GB/s", "frac": round(merge_bytes / merge_ms / 1e6 / PEAK_HBM_GBS, 4),
                            "traffic": None, "algorithmic_bytes": merge_bytes, "kernel": f"merge_kernel<{D}>"},
