@@ -26,8 +26,10 @@
  * text (causal) and image (full) segments, and only a suffix of it may be
  * queried, with Q and O holding just the queried rows. With
  * pva_seg_desc_build_kv_chunk, K and V may hold just a chunk of each
- * sequence's keys; packed_attn_fwd_partial then also returns the rows'
- * log-sum-exp and pva_merge_partials combines the chunks' results.
+ * sequence's keys; packed_attn_fwd_partial (bf16) or
+ * packed_attn_fwd_partial_fp8 then also returns the rows' log-sum-exp and
+ * pva_merge_partials combines the chunks' results. packed_attn_fwd_paged
+ * reads K and V from a block pool through a block table.
  *
  * Ownership: the caller owns every tensor and every stream. The library owns
  * only a pva_seg_desc (host copy + device work list), freed by
