@@ -205,9 +205,12 @@ void pva_seg_desc_free(pva_seg_desc* desc);
  *   scale      : softmax scale (finite, > 0), usually 1/sqrt(D)
  *   out        : device bf16 [N, H, D], 16-byte aligned; every row of every
  *                sequence is written; nothing outside [N, H, D] is touched
- *   stream     : hipStream_t to launch on (NULL = null stream)
+ *   stream     : hipStream_t to launch on (NULL = null stream), a stream of
+ *                the current device
  * The descriptor may come from either builder as long as every q_start is 0
- * (else PVA_ERR_INVALID_ARG: use packed_attn_fwd_varlen).
+ * (else PVA_ERR_INVALID_ARG: use packed_attn_fwd_varlen). Every forward
+ * entry point requires the current device to be the one the descriptor was
+ * built on (its work list lives there); else PVA_ERR_INVALID_ARG.
  * Asynchronous; allocates nothing. With the environment variable PVA_CHECK=1
  * the device cu_seqlens is copied back (synchronously) and compared with the
  * descriptor's before the launch.

@@ -72,6 +72,12 @@ int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu_
   if (d->plan.dtype != want)
     return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built for another dtype");
   if (!d->d_items) return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built host-only and cannot be launched");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_error(e, "hipGetDevice");
+  if (dev != d->device)
+    return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built on device " + std::to_string(d->device) +
+                                              " but the current device is " + std::to_string(dev));
   return PVA_OK;
 }
 
