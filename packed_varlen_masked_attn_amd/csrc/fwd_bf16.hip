@@ -338,12 +338,16 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
     if (paged) {
       blk = min(max(blk, 0), pg.num_blocks - 1);
       const int row = k0 & ((1 << pg.block_shift) - 1);
-      bytes = uint32_t(min(BN, L - k0) - 1) * rs2 + 2u * D;  // rows of the sequence in this tile
+      // the rows of the sequence in this tile; none for a tile past its end
+      // (rs2 >= 2 D makes the expression negative there; the scalar read
+      // keeps the range in scalar registers)
+      bytes = uint32_t(__builtin_amdgcn_readfirstlane(max(min(BN, L - k0) * int(rs2) - int(rs2) + 2 * D, 0)));
       return reinterpret_cast<const uint8_t*>(contiguous + ((int64_t(blk) << pg.block_shift) + row) * rs +
                                               int64_t(it.head) * D);
     } else {
       const uint32_t o = uint32_t(k0) * rs2;
-      bytes = head_bytes - o;
+      // nothing for a tile past the sequence end
+      bytes = head_bytes - uint32_t(__builtin_amdgcn_readfirstlane(min(o, head_bytes)));
       return reinterpret_cast<const uint8_t*>(contiguous + base) + o;
     }
   };
@@ -357,13 +361,17 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
     const uint8_t* src = tile_src(V, t, blk, bytes);
     vld.load(make_rsrc(src, bytes), stage, wave);
   };
-  if (kend > 0) ld_k(0, kst[0], block_of(0));
-  if (kend > 1) ld_k(1, kst[1], block_of(1));
-  if (kend > 0) ld_v(0, vst[0], block_of(0));
-  if (kend > 2) ld_k(2, kst[2], block_of(2));
-  if (kend > 1) ld_v(1, vst[1], block_of(1));
-  if (kend > 3) ld_k(3, kst[3], block_of(3));
-  if (kend > 2) ld_v(2, vst[2], block_of(2));
+  // Every tile load is issued whatever kend is (a tile past the sequence end
+  // reads as zeros and touches no memory): each wave then has the same loads
+  // in flight on every path, and the partial vmcnt waits below are exact
+  // also for the compiler, which otherwise guards LDS reads with full waits.
+  ld_k(0, kst[0], block_of(0));
+  ld_k(1, kst[1], block_of(1));
+  ld_v(0, vst[0], block_of(0));
+  ld_k(2, kst[2], block_of(2));
+  ld_v(1, vst[1], block_of(1));
+  ld_k(3, kst[3], block_of(3));
+  ld_v(2, vst[2], block_of(2));
   // pool blocks of the tiles the first loop iteration loads
   int kblk = block_of(NS), vblk = block_of(NS - 1);
 
@@ -387,10 +395,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   ra.init(l32, g, 4 * g + (lane & 15) / 4, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
   // K0, K1, V0 must have landed; K2 V1 K3 V2 may still be in flight
-  if (kend > 3)
-    wait_vmcnt<2 * Cfg::DMA_MIN>();
-  else
-    wait_vmcnt<0>();
+  wait_vmcnt<2 * Cfg::DMA_MIN>();
   lds_barrier();
 
   f32x16 sa, sb;
@@ -411,9 +416,8 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   auto iteration = [&](auto sj_tag, int j, f32x16& scur, f32x16& snext) {
     constexpr int SJ = decltype(sj_tag)::value;
     lds_barrier();  // every wave is done with S(j) (K stage SJ) and PV(j-1) (V stage SJ-1)
-    const bool steady = j + NS < kend;
-    if (steady) ld_k(j + NS, kst[SJ], kblk);
-    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS], vblk);
+    ld_k(j + NS, kst[SJ], kblk);
+    ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS], vblk);
     if constexpr (PAGED) {  // the next iteration's blocks, read ahead
       kblk = block_of(j + NS + 1);
       vblk = block_of(j + NS);
@@ -441,11 +445,8 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
       st.m = need ? mt : st.m;
     }
     // K(j+2) and V(j+1) are needed next; the loads of iterations j-1 and j
-    // may stay in flight in steady state
-    if (steady)
-      wait_vmcnt<2 * Cfg::DMA_MIN>();
-    else
-      wait_vmcnt<0>();
+    // may stay in flight
+    wait_vmcnt<2 * Cfg::DMA_MIN>();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -464,6 +465,10 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
     if (j + 3 >= kend) break;
     iteration(I3{}, j + 3, sb, sa);
   }
+
+  // the loads of the last iterations (tiles past kend) must land before the
+  // workgroup ends and its LDS is handed to another
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l (bf16, or fp32 for partial results), rows of
   // this tile only; optionally the row's log-sum-exp of the scaled scores,
