@@ -300,21 +300,28 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   // sequence: rows past the end read as zeros
   kld.init(rs32, lane, wave);
   vld.init(rs32, lane, wave);
+  // (a tile past the sequence end gets an empty range: it reads as zeros and
+  // touches no memory; the scalar read keeps the range in scalar registers)
+  auto tile_bytes = [&](uint32_t o) { return head_bytes - uint32_t(__builtin_amdgcn_readfirstlane(min(o, head_bytes))); };
   auto ld_k = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs32;
-    kld.load(make_rsrc(Kb + o, head_bytes - o), stage, wave);
+    kld.load(make_rsrc(Kb + o, tile_bytes(o)), stage, wave);
   };
   auto ld_v = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs32;
-    vld.load(make_rsrc(Vb + o, head_bytes - o), stage, wave);
+    vld.load(make_rsrc(Vb + o, tile_bytes(o)), stage, wave);
   };
-  if (kend > 0) ld_k(0, kst[0]);
-  if (kend > 1) ld_k(1, kst[1]);
-  if (kend > 0) ld_v(0, vst[0]);
-  if (kend > 2) ld_k(2, kst[2]);
-  if (kend > 1) ld_v(1, vst[1]);
-  if (kend > 3) ld_k(3, kst[3]);
-  if (kend > 2) ld_v(2, vst[2]);
+  // Every tile load is issued whatever kend is: each wave then has the same
+  // loads in flight on every path, and the partial vmcnt waits below are
+  // exact also for the compiler, which otherwise guards LDS reads with full
+  // waits.
+  ld_k(0, kst[0]);
+  ld_k(1, kst[1]);
+  ld_v(0, vst[0]);
+  ld_k(2, kst[2]);
+  ld_v(1, vst[1]);
+  ld_k(3, kst[3]);
+  ld_v(2, vst[2]);
 
   // Q^T operands: step c holds d = 64 c + 32 g .. +31 of this lane's query row
   i32x8 qf[NKS];
@@ -344,10 +351,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   typename Kn::KAddr kad;
   kad.init(l32, g);
 
-  if (kend > 3)
-    wait_vmcnt<2 * Cfg::DMA_MIN>();
-  else
-    wait_vmcnt<0>();
+  wait_vmcnt<2 * Cfg::DMA_MIN>();
   lds_barrier();
 
   auto s_mfma = [&](f32x16(&s)[NB], const uint8_t* kt) {
@@ -371,9 +375,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[NB], f32x16(&snext)[NB]) {
     constexpr int SJ = decltype(sj_tag)::value;
     lds_barrier();
-    const bool steady = j + NS < kend;
-    if (steady) ld_k(j + NS, kst[SJ]);
-    if (j + NS - 1 < kend) ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
+    ld_k(j + NS, kst[SJ]);
+    ld_v(j + NS - 1, vst[(SJ + NS - 1) % NS]);
     const int k1 = (j + 1) * BN;
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
@@ -396,10 +399,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
       m_run = need ? mt : m_run;
     }
-    if (steady)
-      wait_vmcnt<2 * Cfg::DMA_MIN>();
-    else
-      wait_vmcnt<0>();
+    wait_vmcnt<2 * Cfg::DMA_MIN>();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -418,6 +418,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     if (j + 3 >= kend) break;
     iteration(I3{}, j + 3, sb, sa);
   }
+
+  // the loads of the last iterations (tiles past kend) must land before the
+  // workgroup ends and its LDS is handed to another
+  wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T * v_s / l (l from the ones block), bf16, or fp32
   // for partial results; optionally the row's log-sum-exp of the scaled
