@@ -73,6 +73,10 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of --kernel-only runs "
                          "(no GPU needed) and print the traffic record for --workload")
+    ap.add_argument("--counter-summary", nargs=2, metavar=("SQ_CSV", "UTIL_CSV"),
+                    help="summarise a rocprofv3 counter file of a --kernel-only run (MFMA busy and co-issue "
+                         "cycles, LDS bank conflicts, L2 hits, instruction counts) and one of the derived "
+                         "MfmaUtil counter (no GPU needed); prints the counter record for --workload")
     return ap.parse_args()
 
 
@@ -133,6 +137,82 @@ def pmc_summary(args):
     print("\n".join(lines))
 
 
+# MI355X: 256 CUs of 4 SIMDs in 8 XCDs; GRBM_GUI_ACTIVE is summed over the XCDs
+NUM_SIMD, NUM_XCD = 1024, 8
+SQ_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_LDS_BANK_CONFLICT",
+               "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU",
+               "GRBM_GUI_ACTIVE", "TCC_HIT_sum", "TCC_MISS_sum")
+
+
+def counters_file(dtype, workload):
+    return os.path.join(PROFILES, f"counters_fwd_{dtype}_{workload}.txt")
+
+
+def counter_summary(args):
+    """MFMA busy share, co-issued VALU cycles, LDS bank-conflict cycles, L2 hit
+    rate and instruction mix of the attention kernel, from one rocprofv3 --pmc
+    run over the SQ/GRBM/TCC counters and one over the derived MfmaUtil."""
+    import csv
+    sq_csv, util_csv = args.counter_summary
+    w = workloads.WORKLOADS[args.workload]()
+    dtype = "fp8" if w.dtype == "fp8" else "bf16"
+    tag = f"fwd_{dtype}_kernel"
+    vals, durations = {}, {}
+    with open(sq_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            if tag not in row["Kernel_Name"]:
+                continue
+            vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+            durations[row["Dispatch_Id"]] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+    missing = [c for c in SQ_COUNTERS if c not in vals]
+    util = [v for k, v in _counter_rows(util_csv, "MfmaUtil") if tag in k]
+    if missing or not util:
+        sys.exit(f"counter summary: no {tag} dispatch with {missing or ['MfmaUtil']}")
+    m = {c: statistics.fmean(v) for c, v in vals.items()}
+    cycles = m["GRBM_GUI_ACTIVE"] / NUM_XCD  # shader cycles per launch (per XCD)
+    busy = m["SQ_VALU_MFMA_BUSY_CYCLES"]
+    lines = [
+        f"kernel: {tag}",
+        f"workload: {w.name}",
+        f"source_sha256_16: {kernel_source_hash(dtype)}",
+        f"dispatches: {len(vals['GRBM_GUI_ACTIVE'])}",
+        f"shader_cycles_per_launch: {cycles:.0f}",
+        f"shader_clock_ghz_fastest_dispatch: {cycles / min(durations.values()):.3f}",
+        f"mfma_busy_pct: {100.0 * busy / (NUM_SIMD * cycles):.1f}",
+        f"mfma_util_derived_pct: {statistics.fmean(util):.1f}",
+        f"valu_coissue_pct_of_mfma_busy: {100.0 * m['SQ_VALU_MFMA_COEXEC_CYCLES'] / busy:.1f}",
+        f"mfma_cycles_per_instruction: {busy / m['SQ_INSTS_MFMA']:.1f}",
+        f"mfma_instructions_per_launch: {m['SQ_INSTS_MFMA']:.0f}",
+        f"valu_instructions_per_mfma: {m['SQ_INSTS_VALU'] / m['SQ_INSTS_MFMA']:.2f}",
+        f"lds_bank_conflict_cycles: {m['SQ_LDS_BANK_CONFLICT']:.0f}",
+        f"lds_active_cycles: {m['SQ_ACTIVE_INST_LDS']:.0f}",
+        f"l2_hit_pct: {100.0 * m['TCC_HIT_sum'] / (m['TCC_HIT_sum'] + m['TCC_MISS_sum']):.1f}",
+    ]
+    print("\n".join(lines))
+
+
+def stored_counters(dtype, workload):
+    """Counter record for this kernel and workload if taken on the current
+    sources, else None."""
+    path = counters_file(dtype, workload)
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    if rec.get("source_sha256_16") != kernel_source_hash(dtype):
+        return None
+    keys = ("mfma_busy_pct", "valu_coissue_pct_of_mfma_busy", "valu_instructions_per_mfma",
+            "lds_bank_conflict_cycles", "l2_hit_pct", "shader_clock_ghz_fastest_dispatch")
+    try:
+        return {k: float(rec[k]) for k in keys}
+    except (KeyError, ValueError):
+        return None
+
+
 def algorithmic_bytes(w):
     """Q, K, V read once and O written once (fp8: 1-byte inputs, bf16 output),
     plus the per-(sequence, head) scales of the fp8 path. Q and O hold the
@@ -187,6 +267,9 @@ def main():
 
     if args.pmc_summary:
         pmc_summary(args)
+        return
+    if args.counter_summary:
+        counter_summary(args)
         return
 
     import torch
@@ -342,6 +425,11 @@ def main():
         "kernel": ("fwd_fp8_kernel<128>" if is_fp8 else f"fwd_bf16_kernel<{D}>") + (" (paged K/V)" if args.paged else ""),
         "algorithmic_bytes": algorithmic_bytes(w),
     }
+    if result["roofline"]["traffic"]:
+        result["roofline"]["hbm_gbs"] = round(result["roofline"]["traffic"] / (k_avg * 1e-3) / 1e9, 1)
+    ctr = None if args.paged else stored_counters(dtype, w.name)
+    if ctr:
+        result["counters"] = ctr
     if args.kernel_only:
         print(json.dumps(result), flush=True)
         return

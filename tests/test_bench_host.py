@@ -1,4 +1,4 @@
-"""Host-side pieces of bench.py: the single-GPU guard and the HBM counter summary."""
+"""Host-side pieces of bench.py: the single-GPU guard and the rocprofv3 counter summaries."""
 import csv
 import os
 import subprocess
@@ -70,3 +70,41 @@ def test_algorithmic_bytes():
     assert bench.algorithmic_bytes(w) == 4 * 2 * 25072 * 32 * 128
     w8 = workloads.WORKLOADS["mixed_res_fp8"]()
     assert bench.algorithmic_bytes(w8) == 5 * 25072 * 32 * 128 + 12 * 8 * 32
+
+
+def test_counter_summary_ratios(tmp_path, capsys):
+    k = "_ZN3pva12_GLOBAL__N_115fwd_bf16_kernelILi128EEEv"
+    cycles = 1000.0  # per XCD
+    vals = {"GRBM_GUI_ACTIVE": 8 * cycles, "SQ_VALU_MFMA_BUSY_CYCLES": 0.5 * 1024 * cycles,
+            "SQ_VALU_MFMA_COEXEC_CYCLES": 0.25 * 1024 * cycles, "SQ_INSTS_MFMA": 1024 * cycles / 64,
+            "SQ_INSTS_VALU": 5 * 1024 * cycles / 64, "SQ_LDS_BANK_CONFLICT": 7.0, "SQ_ACTIVE_INST_LDS": 1.0,
+            "SQ_ACTIVE_INST_VALU": 1.0, "SQ_BUSY_CYCLES": 1.0, "TCC_HIT_sum": 900.0, "TCC_MISS_sum": 100.0}
+    _csv(tmp_path / "sq.csv", [("other", "SQ_INSTS_MFMA", 1e9)] + [(k, c, v) for c, v in vals.items()])
+    _csv(tmp_path / "u.csv", [(k, "MfmaUtil", 49.0)])
+
+    class A:
+        workload = "tiny"
+        counter_summary = [str(tmp_path / "sq.csv"), str(tmp_path / "u.csv")]
+    bench.counter_summary(A)
+    rec = dict(line.split(": ", 1) for line in capsys.readouterr().out.strip().splitlines())
+    assert float(rec["mfma_busy_pct"]) == pytest.approx(50.0)
+    assert float(rec["valu_coissue_pct_of_mfma_busy"]) == pytest.approx(50.0)
+    assert float(rec["mfma_cycles_per_instruction"]) == pytest.approx(32.0)
+    assert float(rec["valu_instructions_per_mfma"]) == pytest.approx(5.0)
+    assert float(rec["l2_hit_pct"]) == pytest.approx(90.0)
+    assert float(rec["lds_bank_conflict_cycles"]) == 7.0
+    assert float(rec["mfma_util_derived_pct"]) == pytest.approx(49.0)
+
+
+def test_stored_counters_require_current_sources(tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    path = bench.counters_file("fp8", "wl")
+    body = ("mfma_busy_pct: 47.4\nvalu_coissue_pct_of_mfma_busy: 55.0\nvalu_instructions_per_mfma: 15.67\n"
+            "lds_bank_conflict_cycles: 0\nl2_hit_pct: 92.1\nshader_clock_ghz_fastest_dispatch: 1.924\n")
+    with open(path, "w") as f:
+        f.write(f"# comment: ignored\nsource_sha256_16: {bench.kernel_source_hash('fp8')}\n" + body)
+    assert bench.stored_counters("fp8", "wl")["mfma_busy_pct"] == 47.4
+    with open(path, "w") as f:
+        f.write("source_sha256_16: 0000000000000000\n" + body)
+    assert bench.stored_counters("fp8", "wl") is None
+    assert bench.stored_counters("bf16", "missing") is None
