@@ -227,6 +227,29 @@ def draw_f32(w: Workload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     return q, k, v
 
 
+def drift_f32(w: Workload, q_bias: float, k_ramp: float, spike: float = 0.0
+              ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Inputs whose scores rise along the keys, for the running maximum of an
+    online softmax: the draws of ``draw_f32`` with ``q_bias`` added to every
+    query element and ``k_ramp * j / (L - 1)`` added to every element of key
+    row j of each sequence (length L). A query's score then drifts upwards by
+    about sqrt(D) * q_bias * k_ramp over the sequence at softmax scale
+    1/sqrt(D). With ``spike`` > 0, the even-indexed sequences also get
+    ``spike`` added to every element of one key row three quarters into
+    their image block (the rows that see it jump by about
+    sqrt(D) * q_bias * spike there)."""
+    q, k, v = draw_f32(w)
+    q += np.float32(q_bias)
+    a = 0
+    for s, (t, n) in enumerate(zip(w.text_len, w.seq_len)):
+        if n > 1:
+            k[a:a + n] += (np.float32(k_ramp) * np.arange(n, dtype=np.float32) / np.float32(n - 1))[:, None, None]
+        if spike > 0 and s % 2 == 0 and n > t:
+            k[a + t + 3 * (n - t) // 4] += np.float32(spike)
+        a += n
+    return q, k, v
+
+
 def to_bf16(x: np.ndarray):
     """Round-to-nearest-even cast of a float32 array to a CPU torch bf16 tensor."""
     import torch
