@@ -40,6 +40,19 @@ namespace {
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
+// Probabilities are quantised to E4M3 as p = 2^(score - m + kP8Shift), m the
+// row's reference max (log2 units), which is raised whenever a tile's max
+// exceeds it by more than kP8Lazy. So p stays at or below 2^8.75 < 448
+// (E4M3's largest finite value), and a row's largest p is at least
+// 2^kP8Shift: keys up to 10 log2 units below the row max keep E4M3's normal
+// range (2^-6 and up, 2^-4 relative rounding) instead of 6 with p_max = 1;
+// below it the spacing is a fixed 2^-9, a large relative error on
+// probabilities that still carry mass when the scores spread widely. The
+// shift cancels in O / l.
+constexpr float kP8Shift = 4.0f;
+constexpr float kP8Lazy = 4.75f;
+static_assert(kP8Shift + kP8Lazy < 8.807f, "largest probability below 448");
+
 struct Fp8Cfg {
   static constexpr int D = 128;
   static constexpr int BM = 128, BN = 64, NW = 4, NT = 256;
@@ -340,6 +353,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   i32x8 ones;
 #pragma unroll
   for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;  // E4M3 1.0 in every byte
+  // reference max of the row (log2 units); the probabilities are
+  // p = 2^(score - m_run + kP8Shift), see kP8Shift
   float m_run = -INFINITY;
 
   // per-lane constant parts of the V^T transpose-read addresses: this lane
@@ -380,7 +395,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     const int k1 = (j + 1) * BN;
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
-    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run, pb, kad);
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run - kP8Shift, pb, kad);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
     const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, scale_log2, vrow0, vsw, half, p8);
@@ -389,8 +404,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     // lo = q(p - hi), through a second PV pass: hi + lo carries p to about
     // 2^-8 relative instead of 2^-4. S(j) is still live here.
     if (__builtin_expect(k1 > wlim_min, 0))
-      Kn::pv_residual(oacc, vst[SJ], scur, scale_log2, m_run, pb, ones, vrow0, vsw, half, p8);
-    const bool need = mt > m_run + kLazyRescale;
+      Kn::pv_residual(oacc, vst[SJ], scur, scale_log2, m_run - kP8Shift, pb, ones, vrow0, vsw, half, p8);
+    const bool need = mt > m_run + kP8Lazy;
     if (__builtin_expect(wave_any(need), 0)) {
       const float alpha = need ? fast_exp2(m_run - mt) : 1.0f;
 #pragma unroll
@@ -425,7 +440,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
 
   // ---- epilogue: O = O^T * v_s / l (l from the ones block), bf16, or fp32
   // for partial results; optionally the row's log-sum-exp of the scaled
-  // scores, ln 2 * (m + log2 l) with l the sum of the weights PV applied
+  // scores, ln 2 * (m + log2 l - kP8Shift) with l the sum of the weights PV applied
   // (-inf for a row with no key in range)
   if (wave_active && qrow < qend) {
     const float lt = oacc[NDB][0];
@@ -456,7 +471,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     }
     if (lse && g == 0)
       lse[int64_t(it.qo_row - it.q0 + qrow) * H + it.head] =
-          lt > 0.0f ? 0.6931471805599453f * (m_run + __log2f(lt)) : -INFINITY;
+          lt > 0.0f ? 0.6931471805599453f * (m_run - kP8Shift + __log2f(lt)) : -INFINITY;
   }
 }
 

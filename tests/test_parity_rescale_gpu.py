@@ -124,3 +124,53 @@ def test_partial_lse_score_drift():
     say(f"[rescale] partial: O max {mx:.3e} mean {mean:.3e}, lse max {lmx:.3e}")
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
     assert lmx <= LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("scale", [1e-3, 0.5, 1.0])
+def test_bf16_softmax_scales(scale):
+    """Other softmax scales on N(0,1) inputs: near-uniform weights (1e-3) and
+    peaked ones whose scores spread over tens of log2 units (0.5, 1), where
+    the reference max moves and most probabilities underflow."""
+    w = workloads.custom([150, 150], [900, 900], 2, 128, seed=5700)
+    out, q, k, v, _ = run_bf16(w, scale=scale)
+    ref = oracle.packed_attention(f64(q), f64(k), f64(v), w.text_len, w.image_len, scale)
+    mx, mean = err_stats(f64(out), ref)
+    say(f"[scale] bf16 scale={scale}: max {mx:.3e} mean {mean:.3e}")
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
+
+
+# Peaked softmax in fp8: when two keys carry most of a row's weight (w, 1 - w),
+# rounding both probabilities to E4M3 (relative error up to 2^-4 each, the
+# row sum taken over the rounded values) moves the output by
+# w (1 - w) (e1 - e2) (v1 - v2), at most 2^-2 * 2^-3 * |v1 - v2|. Over about a
+# million N(0,1) output elements |v1 - v2| reaches about 5, so the max bound
+# is 0.16; the mean of that term is at most 2^-2 * (2/3) 2^-4 * 2/sqrt(pi),
+# 1.2e-2, reached only if every row were a two-key mixture.
+FP8_PEAKED_MAX = 0.16
+FP8_PEAKED_MEAN = 1.2e-2
+
+
+def _fp8_scale_run(scale):
+    from gpu_util import run_fp8
+    w = workloads.custom([150, 150], [900, 900], 2, 128, seed=5800, dtype="fp8")
+    out, q, k, v, _ = run_fp8(w, scale=scale)
+    ref = oracle.packed_attention(q, k, v, w.text_len, w.image_len, scale)
+    mx, mean = err_stats(f64(out), ref)
+    say(f"[scale] fp8 scale={scale}: max {mx:.3e} mean {mean:.3e}")
+    assert np.all(np.isfinite(f64(out)))
+    return mx, mean
+
+
+@pytest.mark.parametrize("scale", [1e-3, 0.2])
+def test_fp8_softmax_scales(scale):
+    """Near-uniform weights, and scores spread widely enough that much of a
+    row's weight sits 6-10 log2 units below its max (E4M3's subnormal range
+    unless the probabilities are shifted up): the fp8 bound of 6e-2."""
+    mx, mean = _fp8_scale_run(scale)
+    assert mx <= FP8_MAX_ABS, (mx, mean)
+
+
+@pytest.mark.parametrize("scale", [0.35, 0.5, 1.0])
+def test_fp8_peaked_softmax(scale):
+    mx, mean = _fp8_scale_run(scale)
+    assert mx <= FP8_PEAKED_MAX and mean <= FP8_PEAKED_MEAN, (mx, mean)
