@@ -14,6 +14,7 @@ Prints ONE JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import gc
 import json
 import math
 import os
@@ -368,6 +369,10 @@ def main():
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     torch.cuda.synchronize()
+    # Python's cyclic garbage collector is kept out of the timed region (as
+    # timeit does): a full collection stalls the launching thread for tens of
+    # milliseconds, and the GPU runs dry meanwhile
+    gc.disable()
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         starts[i].record(stream)
@@ -375,6 +380,7 @@ def main():
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
+    gc.enable()
     kms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms_per_step = wall * 1e3 / args.steps
     value = flops * args.steps / wall / 1e12
@@ -496,13 +502,14 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     out = torch.empty((N, H, D), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
+    part_out = [(o_parts[p], l_parts[p]) for p in range(P)]
+
     def step(ev=None):
-        for p, (d, kp, vp, cuk) in enumerate(parts):
+        for (d, kp, vp, cuk), (op, lp) in zip(parts, part_out):
             if fp8_scales is not None:
-                pva.packed_attn_fwd_partial_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, o_parts[p], l_parts[p],
-                                                stream)
+                pva.packed_attn_fwd_partial_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, op, lp, stream)
             else:
-                pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, o_parts[p], l_parts[p], stream)
+                pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, op, lp, stream)
         if ev is not None:
             ev.record(stream)
         pva.merge_partials(o_parts, l_parts, out, None, stream)
@@ -513,6 +520,7 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     t0s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     mids = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
     t1s = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    gc.disable()  # as in the main timed region
     t_wall0 = time.perf_counter()
     for i in range(args.steps):
         t0s[i].record(stream)
@@ -520,12 +528,16 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
         t1s[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
-    part_ms = statistics.fmean(a.elapsed_time(b) for a, b in zip(t0s, mids))
-    merge_ms = statistics.fmean(a.elapsed_time(b) for a, b in zip(mids, t1s))
+    gc.enable()
+    parts_all = [a.elapsed_time(b) for a, b in zip(t0s, mids)]
+    merges_all = [a.elapsed_time(b) for a, b in zip(mids, t1s)]
+    part_ms = statistics.fmean(parts_all)
+    merge_ms = statistics.fmean(merges_all)
     ms_per_step = wall * 1e3 / args.steps
     value = flops * args.steps / wall / 1e12
     merge_bytes = N * H * (P * (4 * D + 4) + 2 * D)
-    log(f"[bench] split keys x{P}: {ms_per_step:.4f} ms/step (partials {part_ms:.4f} ms, merge {merge_ms:.4f} ms) "
+    log(f"[bench] split keys x{P}: {ms_per_step:.4f} ms/step (partials {part_ms:.4f} ms, median "
+        f"{statistics.median(parts_all):.4f}, max {max(parts_all):.4f}; merge {merge_ms:.4f} ms) "
         f"-> {value:.1f} useful TFLOP/s; merge {merge_bytes / merge_ms / 1e6:.0f} GB/s")
     achieved = flops / (part_ms * 1e-3) / 1e12
     print(json.dumps({
@@ -535,7 +547,10 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
         "dtype": dtype, "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
         "config": {"workload": w.name, "split_keys": P, "text_len": list(w.text_len), "image_len": list(w.image_len),
                    "num_heads": H, "head_dim": D, "parallelism": "single GPU"},
-        "partials_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5), "desc_build_us": round(desc_us, 1),
+        "partials_ms": round(part_ms, 5), "merge_ms": round(merge_ms, 5),
+        "partials_ms_median_p90": [round(statistics.median(parts_all), 5), round(pct(parts_all, 90), 5)],
+        "merge_ms_median_p90": [round(statistics.median(merges_all), 5), round(pct(merges_all, 90), 5)],
+        "desc_build_us": round(desc_us, 1),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS[dtype], 4), "traffic": None,
                      "kernel": ("fwd_fp8_kernel" if dtype == "fp8" else f"fwd_bf16_kernel<{D}>") +

@@ -32,22 +32,46 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ o_
   const int64_t row = int64_t(blockIdx.x) * (256 / TPR) + threadIdx.x / TPR;
   if (row >= rows) return;
   const int col = 4 * (threadIdx.x % TPR);
+  // every part's lse and O slice is loaded before any is used, four parts
+  // at a time, so that each lane keeps several 16-byte loads in flight (the
+  // partial results are read once: non-temporal loads)
+  constexpr int U = 4;
   float top = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) top = fmaxf(top, lse_parts[int64_t(p) * rows + row]);
+  f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  for (int p0 = 0; p0 < n_parts; p0 += U) {
+    float lp[U];
+    f32x4 o[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int p = p0 + u;
+      lp[u] = p < n_parts ? __builtin_nontemporal_load(lse_parts + int64_t(p) * rows + row) : -INFINITY;
+      o[u] = p < n_parts ? __builtin_nontemporal_load(
+                               reinterpret_cast<const f32x4*>(o_parts + (int64_t(p) * rows + row) * D + col))
+                         : f32x4{};
+    }
+    // running max over the parts seen so far; earlier sums are rescaled when it moves
+    float t = top;
+#pragma unroll
+    for (int u = 0; u < U; ++u) t = fmaxf(t, lp[u]);
+    if (t != -INFINITY) {
+      const float r = top == -INFINITY ? 0.0f : __expf(top - t);
+      acc *= r;
+      den *= r;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const float w = lp[u] == -INFINITY ? 0.0f : __expf(lp[u] - t);
+        acc += w * o[u];
+        den += w;
+      }
+      top = t;
+    }
+  }
   bf16x4 res;
   float lse = -INFINITY;
   if (top == -INFINITY) {
     res = bf16x4{};
   } else {
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    float den = 0.0f;
-    for (int p = 0; p < n_parts; ++p) {
-      const float lp = lse_parts[int64_t(p) * rows + row];
-      const float w = lp == -INFINITY ? 0.0f : __expf(lp - top);
-      const f32x4 o = *reinterpret_cast<const f32x4*>(o_parts + (int64_t(p) * rows + row) * D + col);
-      acc += w * o;
-      den += w;
-    }
     const float inv = 1.0f / den;
 #pragma unroll
     for (int e = 0; e < 4; ++e) res[e] = (__bf16)(acc[e] * inv);
