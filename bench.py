@@ -444,6 +444,7 @@ def main():
     if args.cold_iters > 0:
         scratch = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
         cms = []
+        gc.disable()
         for i in range(args.cold_iters):
             scratch.fill_(float(i))
             s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -452,6 +453,7 @@ def main():
             e.record(stream)
             e.synchronize()
             cms.append(s.elapsed_time(e))
+        gc.enable()
         del scratch
         cmed = statistics.median(cms)
         result["cold"] = {"median_ms": round(cmed, 5), "p10_ms": round(pct(cms, 10), 5),
