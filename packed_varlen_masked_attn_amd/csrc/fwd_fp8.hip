@@ -15,9 +15,11 @@
 //                           A = K from LDS (two 16-byte reads per lane),
 //                           B = Q^T in registers for the whole item.
 //   softmax in fp32, log2 domain, with the score scale q_s * k_s * scale
-//   folded into the exponent; lazy rescaling as in the bf16 kernel.
+//   folded into the exponent; lazy rescaling as in the bf16 kernel, with a
+//   lower threshold and the probabilities shifted up by a power of two
+//   (kP8Shift below) so that they use E4M3's normal range.
 //   P is quantised to E4M3 (round to nearest even) straight from the S^T
-//   accumulators into the B operand of PV; probabilities stay <= 2^8, well
+//   accumulators into the B operand of PV; probabilities stay <= 2^8.75,
 //   inside the format's range.
 //   O^T[d, q] += V^T P^T    A = V^T read with ds_read_b64_tr_b8 (8 keys of
 //                           one column per read); a fifth 32-row block whose A
