@@ -83,3 +83,11 @@ def test_fp8_first_text_row_is_v0():
     for s in range(w.nseq):
         ref = v[off[s]]
         assert np.max(np.abs(got[off[s]] - ref) / np.maximum(np.abs(ref), 1e-3)) <= 2 ** -8
+
+
+def test_fp8_many_sequences():
+    rng = np.random.default_rng(6300)
+    t, i = workloads.random_lengths(rng, 20, 160, 320)
+    t = (1, 1, 0, 0, 63, 63) + t
+    i = (0, 0, 1, 1, 65, 65) + i
+    _full(workloads.custom(t, i, 2, 128, seed=6400, dtype="fp8"), "many sequences")

@@ -179,3 +179,16 @@ def test_device_cu_seqlens_check(monkeypatch):
     good = torch.from_numpy(desc.cu_seqlens).cuda()
     pva.packed_attn_fwd(q, k, v, good, desc, 0.125, torch.empty_like(q))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_many_sequences(D):
+    """Twenty CFG pairs of random lengths (empty text or image blocks, single
+    tokens, lengths around tile edges) in one pack: hundreds of work items of
+    every class, placed by the scheduler across the XCDs."""
+    rng = np.random.default_rng(6100 + D)
+    t, i = workloads.random_lengths(rng, 20, 160, 320)
+    # a few fixed awkward lengths among the random ones
+    t = (1, 1, 0, 0, 127, 127) + t
+    i = (0, 0, 1, 1, 129, 129) + i
+    _full_compare(workloads.custom(t, i, 2, D, seed=6200 + D), f"many sequences D={D}")
