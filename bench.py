@@ -81,12 +81,39 @@ def parse():
     return ap.parse_args()
 
 
+def code_tokens(text):
+    """C/C++ source without its comments and with whitespace runs collapsed
+    (string and character literals kept as written), so that editing a
+    comment does not count as changing the kernel."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_hash(dtype):
+    """Hash of the code (not the comments) of the kernel's sources and the planner."""
     import hashlib
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[dtype]:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode() + b"\0" + code_tokens(f.read()).encode())
     return h.hexdigest()[:16]
 
 

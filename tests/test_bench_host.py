@@ -108,3 +108,10 @@ def test_stored_counters_require_current_sources(tmp_path, monkeypatch):
         f.write("source_sha256_16: 0000000000000000\n" + body)
     assert bench.stored_counters("fp8", "wl") is None
     assert bench.stored_counters("bf16", "missing") is None
+
+
+def test_source_hash_ignores_comments():
+    code = 'int f(int x) { return x + 1; }  // one\n/* two */ const char* s = "a // b";\n'
+    assert bench.code_tokens(code) == bench.code_tokens(code.replace("one", "uno").replace("two", "dos"))
+    assert bench.code_tokens(code) != bench.code_tokens(code.replace("x + 1", "x + 2"))
+    assert '"a // b"' in bench.code_tokens(code)
