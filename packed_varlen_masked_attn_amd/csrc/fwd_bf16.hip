@@ -7,8 +7,8 @@
 // text prefix, bidirectional image block that sees the whole prefix).
 //
 // One workgroup = 4 waves = one work item (sequence, head, 128 query rows);
-// each wave owns 32 query rows, two workgroups share a CU (two waves per
-// SIMD). Keys are streamed in tiles of 32.
+// each wave owns 32 query rows, three workgroups share a CU (three waves
+// per SIMD, at most 168 registers each). Keys are streamed in tiles of 32.
 //
 // Per wave and key tile j, on 32x32x16 bf16 MFMA:
 //   S^T[key, q] = K Q^T    A = K from LDS (16-byte reads), B = Q^T held in
@@ -25,14 +25,14 @@
 // Software pipeline (iteration j, one barrier each):
 //   issue global->LDS loads of K(j+NS) and V(j+NS-1) (buffer loads straight
 //   into LDS; rows past the sequence end read as zeros)
-//   phase 1: [S(j+1) MFMAs] next to [exp / bf16 packing of tile j]; the V^T
-//            operands of PV(j) are read from LDS here as well
+//   phase 1: [S(j+1) MFMAs] next to [exp / bf16 packing of tile j]
 //   (partial tiles only) element mask of tile j+1
-//   phase 2: [PV(j) MFMAs] next to [row sums of tile j, row max of tile j+1]
+//   phase 2: [PV(j) MFMAs] next to [row sums of tile j, row max of tile j+1];
+//            the V^T operands are read from LDS two MFMAs ahead
 //   rare branch: rescale O and l when a row's reference max moved
 //   wait for the loads of K(j+2) and V(j+1) only; later ones stay in flight
-// K and V each have a ring of NS LDS stages, so every load has NS-1
-// iterations to land. Tiles the mask fully hides are never loaded; tiles it
+// K and V each have a ring of NS = 3 LDS stages (48 KB per workgroup), so
+// every load has two iterations to land. Tiles the mask fully hides are never loaded; tiles it
 // fully allows skip the element mask.
 #include <type_traits>
 
@@ -49,7 +49,7 @@ struct Bf16Cfg {
   static constexpr int C = D / 8;          // 16-byte chunks per K/V row
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
-  static constexpr int NS = 4;             // LDS stages per tensor
+  static constexpr int NS = 3;             // LDS stages per tensor
   // K and V tiles are stored unpadded (C 16-byte chunks per row), with the
   // chunks of each row XOR-permuted so that the MFMA operand reads are free of
   // LDS bank conflicts:
@@ -77,7 +77,7 @@ struct Bf16Cfg {
   // the partial vmcnt waits count only these, so waves with more loads in
   // flight simply wait a little longer
   static constexpr int DMA_MIN = KSLOTS / NT + VSLOTS / NT;
-  static_assert(2 * (KTILE + VTILE) * NS <= 160 * 1024, "two workgroups per CU");
+  static_assert(3 * (KTILE + VTILE) * NS <= 160 * 1024, "three workgroups per CU");
 };
 
 __device__ __forceinline__ float max3(float a, float b, float c) {
@@ -143,20 +143,14 @@ struct Kernel {
   // ---- phase 1: S(j+1) = K Q^T (NKC dependent MFMAs), each listed with EPC
   // exponentials of tile j and the bf16 packing of the previous group's
   // (the compiler's scheduler places them).
-  // The K operands are read two chunks ahead. Phase 2's V^T operands are read
-  // here too, half before the first MFMA and half after the second, so that
-  // at most 15 LDS reads are in flight (the wave's LDS counter) and the first
-  // MFMA waits for its own operand only.
+  // The K operands are read two chunks ahead.
   static constexpr int NSTEP = 2 * NDB;
   static __device__ __forceinline__ void s_phase(f32x16& snext, const uint8_t* kst, const bf16x8 (&qf)[NKC],
                                                  const f32x16& scur, float scale_log2, float m, float (&e)[16],
-                                                 uint32_t (&pk)[8], const ReadAddr& ra, s16x8 (&va)[NSTEP],
-                                                 const uint8_t* vst) {
+                                                 uint32_t (&pk)[8], const ReadAddr& ra) {
     bf16x8 ka[3];
     ka[0] = read_k(kst, 0, ra);
     if (NKC > 1) ka[1] = read_k(kst, 1, ra);
-#pragma unroll
-    for (int step = 0; step < NSTEP / 2; ++step) va[step] = read_v_step(vst, step, ra);
     snext = f32x16{};
 #pragma unroll
     for (int c = 0; c < NKC; ++c) {
@@ -167,10 +161,6 @@ struct Kernel {
       if (c > 0) {
 #pragma unroll
         for (int k = (c - 1) * EPC / 2; k < c * EPC / 2; ++k) pk[k] = pack_bf16(e[2 * k], e[2 * k + 1]);
-      }
-      if (c == (NKC > 1 ? 1 : 0)) {
-#pragma unroll
-        for (int step = NSTEP / 2; step < NSTEP; ++step) va[step] = read_v_step(vst, step, ra);
       }
       }
     // consume the results in an empty asm: the compiler must compute them
@@ -188,9 +178,13 @@ struct Kernel {
 
   // ---- phase 2: O^T += V^T P^T (2 NDB MFMAs), each listed with the row-sum
   // dot products of the probabilities and, from the third on, part of the
-  // row max of S(j+1). `va` holds every V^T operand (read in phase 1).
-  static __device__ __forceinline__ void pv_phase(f32x16 (&o)[NDB], const s16x8 (&va)[NSTEP], const float (&e)[16],
-                                                  uint32_t (&pk)[8], const f32x16& snext, float& mx, float& psum) {
+  // row max of S(j+1). The V^T operands are read two steps ahead (holding all
+  // of them from phase 1 on would not fit three waves per SIMD).
+  static __device__ __forceinline__ void pv_phase(f32x16 (&o)[NDB], s16x8 (&va)[NSTEP], const float (&e)[16],
+                                                  uint32_t (&pk)[8], const f32x16& snext, float& mx, float& psum,
+                                                  const uint8_t* vst, const ReadAddr& ra) {
+    va[0] = read_v_step(vst, 0, ra);
+    va[1] = read_v_step(vst, 1, ra);
     constexpr int PPS = 8 / NSTEP;  // row-sum pairs per step
     constexpr int MAX_FROM = NSTEP > 2 ? 2 : 0;  // S(j+1) is complete two MFMAs in
     float part[2] = {0.0f, 0.0f};
@@ -204,6 +198,7 @@ struct Kernel {
 #pragma unroll
         for (int k = (NKC - 1) * EPC / 2; k < 8; ++k) pk[k] = pack_bf16(e[2 * k], e[2 * k + 1]);
       }
+      if (step + 2 < NSTEP) va[step + 2] = read_v_step(vst, step + 2, ra);
       const int kc = step / NDB, db = step % NDB;
       const i32x4 b = {int(pk[4 * kc]), int(pk[4 * kc + 1]), int(pk[4 * kc + 2]), int(pk[4 * kc + 3])};
       o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, va[step]),
@@ -273,13 +268,13 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   using Cfg = typename Kn::Cfg;
   using s16x8 = typename Kn::s16x8;
   constexpr int BN = Cfg::BN, NKC = Cfg::NKC, NDB = Cfg::NDB, NS = Cfg::NS;
-  static_assert(NS == 4, "the loop below is unrolled for a ring of four stages");
+  static_assert(NS == 3, "the loop below is unrolled for a ring of three stages");
   // separate arrays per stage: the compiler sees that an LDS DMA into one
   // stage and reads of another do not alias
-  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::KTILE], k1s[Cfg::KTILE], k2s[Cfg::KTILE], k3s[Cfg::KTILE];
-  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::VTILE], v1s[Cfg::VTILE], v2s[Cfg::VTILE], v3s[Cfg::VTILE];
-  uint8_t* const kst[NS] = {k0s, k1s, k2s, k3s};
-  uint8_t* const vst[NS] = {v0s, v1s, v2s, v3s};
+  __shared__ __attribute__((aligned(1024))) uint8_t k0s[Cfg::KTILE], k1s[Cfg::KTILE], k2s[Cfg::KTILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t v0s[Cfg::VTILE], v1s[Cfg::VTILE], v2s[Cfg::VTILE];
+  uint8_t* const kst[NS] = {k0s, k1s, k2s};
+  uint8_t* const vst[NS] = {v0s, v1s, v2s};
 
   const WorkItem it = items[blockIdx.x];
   if (it.seq < 0) return;  // empty slot; uniform over the workgroup
@@ -370,8 +365,6 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   ld_v(0, vst[0], block_of(0));
   ld_k(2, kst[2], block_of(2));
   ld_v(1, vst[1], block_of(1));
-  ld_k(3, kst[3], block_of(3));
-  ld_v(2, vst[2], block_of(2));
   // pool blocks of the tiles the first loop iteration loads
   int kblk = block_of(NS), vblk = block_of(NS - 1);
 
@@ -394,8 +387,8 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   typename Kn::ReadAddr ra;
   ra.init(l32, g, 4 * g + (lane & 15) / 4, 16 * ((lane >> 4) & 1) + 4 * (lane & 3));
 
-  // K0, K1, V0 must have landed; K2 V1 K3 V2 may still be in flight
-  wait_vmcnt<2 * Cfg::DMA_MIN>();
+  // K0, K1, V0 must have landed; K2 V1 may still be in flight
+  wait_vmcnt<Cfg::DMA_MIN>();
   lds_barrier();
 
   f32x16 sa, sb;
@@ -423,13 +416,13 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
       vblk = block_of(j + NS);
     }
     const int k1 = (j + 1) * BN;
-    s16x8 va[Kn::NSTEP];  // V^T operands of PV(j), read during phase 1
+    s16x8 va[Kn::NSTEP];  // V^T operands of PV(j), read during phase 2
     float e[16];
     uint32_t pk[8];
-    Kn::s_phase(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st.m, e, pk, ra, va, vst[SJ]);
+    Kn::s_phase(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, st.m, e, pk, ra);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     float mx, psum;
-    Kn::pv_phase(oacc, va, e, pk, snext, mx, psum);
+    Kn::pv_phase(oacc, va, e, pk, snext, mx, psum, vst[SJ], ra);
     st.l += psum;
     const float mt = half_swap_max(mx) * scale_log2;
     const bool need = mt > st.m + kLazyRescale;
@@ -444,26 +437,30 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
       st.l *= alpha;
       st.m = need ? mt : st.m;
     }
-    // K(j+2) and V(j+1) are needed next; the loads of iterations j-1 and j
-    // may stay in flight
-    wait_vmcnt<2 * Cfg::DMA_MIN>();
+    // K(j+2) and V(j+1) are needed next; the loads of iteration j may stay
+    // in flight
+    wait_vmcnt<Cfg::DMA_MIN>();
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  using I3 = std::integral_constant<int, 3>;
 
-  // Four unrolled iterations per trip, each guarded; the last tile's
+  // Six unrolled iterations per trip (two rounds of the three-stage ring, so
+  // that the S buffers alternate), each guarded; the last tile's
   // iteration also computes S of the tile after it on a stale stage, which
   // the mask turns entirely into -inf (no effect on the result).
-  for (int j = 0; j < kend; j += 4) {
+  for (int j = 0; j < kend; j += 6) {
     iteration(I0{}, j, sa, sb);
     if (j + 1 >= kend) break;
     iteration(I1{}, j + 1, sb, sa);
     if (j + 2 >= kend) break;
     iteration(I2{}, j + 2, sa, sb);
     if (j + 3 >= kend) break;
-    iteration(I3{}, j + 3, sb, sa);
+    iteration(I0{}, j + 3, sb, sa);
+    if (j + 4 >= kend) break;
+    iteration(I1{}, j + 4, sa, sb);
+    if (j + 5 >= kend) break;
+    iteration(I2{}, j + 5, sb, sa);
   }
 
   // the loads of the last iterations (tiles past kend) must land before the
@@ -508,7 +505,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
 
 // Two kernels over the same body: K/V contiguous in [N, H, D], or paged.
 template <int D>
-__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(
+__global__ __launch_bounds__(Bf16Cfg<D>::NT, 3) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
     float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse) {
@@ -516,7 +513,7 @@ __global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(Bf16Cfg<D>::NT, 2) void fwd_bf16_paged_kernel(
+__global__ __launch_bounds__(Bf16Cfg<D>::NT, 3) void fwd_bf16_paged_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
     float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse, Paging pg) {
