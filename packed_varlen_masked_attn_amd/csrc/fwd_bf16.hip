@@ -31,9 +31,11 @@
 //            the V^T operands are read from LDS two MFMAs ahead
 //   rare branch: rescale O and l when a row's reference max moved
 //   wait for the loads of K(j+2) and V(j+1) only; later ones stay in flight
-// K and V each have a ring of NS = 3 LDS stages (48 KB per workgroup), so
-// every load has two iterations to land. Tiles the mask fully hides are never loaded; tiles it
-// fully allows skip the element mask.
+// K and V each have a ring of NS = 3 LDS stages (48 KB per workgroup): a
+// load issued at iteration j is waited for at the end of iteration j + 1.
+// Tiles the mask fully hides are never loaded; tiles it fully allows skip
+// the element mask. A wave whose rows all lie past the tile only moves its
+// share of the tiles and meets the barriers.
 #include <type_traits>
 
 #include "kernel_common.h"
