@@ -307,12 +307,16 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   const int wrow0 = it.q0 + 32 * wave;
   const int qrow = wrow0 + l32;
   const int mylim = qrow < qend ? slim[qrow] : L;
-  // a wave whose 32 rows all lie past the tile's last row (in the last tile
-  // of a sequence) only moves its share of the K/V tiles and meets the
-  // barriers (the loop at the end of the tile loop below)
   const bool wave_active = wrow0 < qend;  // uniform per wave: a scalar branch
   const int wlim_min = wave_active ? slim[wrow0] : L;
   const int kend = it.k_end;
+  // The wave's own last key tile: past the key limit of its last row every
+  // tile is fully masked for all its rows (limits never decrease along the
+  // rows). From there on, and for a wave whose rows all lie past the tile
+  // (in the last tile of a sequence), the wave only moves its share of the
+  // K/V tiles and meets the barriers (the loop after the tile loop below).
+  const int wkend =
+      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((slim[min(wrow0 + 31, qend - 1)] + BN - 1) / BN)) : 0;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
   // (tile t's resource starts at key row t * BN and ends with the sequence)
@@ -401,7 +405,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   // S(0) and its reference max. Rows past the sequence end, and tiles past a
   // row's key limit, are computed masked: their probabilities are exactly
   // zero. That keeps every branch in the loop scalar and rare.
-  if (kend > 0 && wave_active) {
+  if (wkend > 0) {
     sa = Kn::s_tile(kst[0], qf, ra);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
     st.m = Kn::tile_max(sa, scale_log2);  // first tile: O and l are still zero
@@ -455,35 +459,33 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   // that the S buffers alternate), each guarded; the last tile's
   // iteration also computes S of the tile after it on a stale stage, which
   // the mask turns entirely into -inf (no effect on the result).
-  if (wave_active) {
-    for (int j = 0; j < kend; j += 6) {
-      iteration(I0{}, j, sa, sb);
-      if (j + 1 >= kend) break;
-      iteration(I1{}, j + 1, sb, sa);
-      if (j + 2 >= kend) break;
-      iteration(I2{}, j + 2, sa, sb);
-      if (j + 3 >= kend) break;
-      iteration(I0{}, j + 3, sb, sa);
-      if (j + 4 >= kend) break;
-      iteration(I1{}, j + 4, sa, sb);
-      if (j + 5 >= kend) break;
-      iteration(I2{}, j + 5, sb, sa);
+  for (int j = 0; j < wkend; j += 6) {
+    iteration(I0{}, j, sa, sb);
+    if (j + 1 >= wkend) break;
+    iteration(I1{}, j + 1, sb, sa);
+    if (j + 2 >= wkend) break;
+    iteration(I2{}, j + 2, sa, sb);
+    if (j + 3 >= wkend) break;
+    iteration(I0{}, j + 3, sb, sa);
+    if (j + 4 >= wkend) break;
+    iteration(I1{}, j + 4, sa, sb);
+    if (j + 5 >= wkend) break;
+    iteration(I2{}, j + 5, sb, sa);
+  }
+  // the rest of the item's tiles: the same barriers and DMA as an iteration
+  // above, none of its arithmetic
+  for (int j = wkend; j < kend; ++j) {
+    lds_barrier();
+    // stage of tile j + 3 (K) and j + 2 (V), picked without indexing the
+    // stage tables at run time
+    const int sk = j % NS, sv = (j + NS - 1) % NS;
+    ld_k(j + NS, sk == 0 ? kst[0] : sk == 1 ? kst[1] : kst[2], kblk);
+    ld_v(j + NS - 1, sv == 0 ? vst[0] : sv == 1 ? vst[1] : vst[2], vblk);
+    if constexpr (PAGED) {
+      kblk = block_of(j + NS + 1);
+      vblk = block_of(j + NS);
     }
-  } else {
-    // the same barriers and DMA as the loop above, none of its arithmetic
-    for (int j = 0; j < kend; ++j) {
-      lds_barrier();
-      // stage of tile j + 3 (K) and j + 2 (V), picked without indexing the
-      // stage tables at run time
-      const int sk = j % NS, sv = (j + NS - 1) % NS;
-      ld_k(j + NS, sk == 0 ? kst[0] : sk == 1 ? kst[1] : kst[2], kblk);
-      ld_v(j + NS - 1, sv == 0 ? vst[0] : sv == 1 ? vst[1] : vst[2], vblk);
-      if constexpr (PAGED) {
-        kblk = block_of(j + NS + 1);
-        vblk = block_of(j + NS);
-      }
-      wait_vmcnt<Cfg::DMA_MIN>();
-    }
+    wait_vmcnt<Cfg::DMA_MIN>();
   }
 
   // the loads of the last iterations (tiles past kend) must land before the
