@@ -308,6 +308,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const bool wave_active = wrow0 < qend;
   const int wlim_min = wave_active ? slim[wrow0] : L;
   const int kend = it.k_end;
+  // the wave's own last key tile (past its last row's key limit every tile is
+  // fully masked for all its rows); 0 for a wave whose rows all lie past the
+  // tile. From there on the wave only moves its share of the K/V tiles and
+  // meets the barriers.
+  const int wkend =
+      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((slim[min(wrow0 + 31, qend - 1)] + BN - 1) / BN)) : 0;
 
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   };
 
   f32x16 sa[NB], sb[NB];
-  if (kend > 0 && wave_active) {
+  if (wkend > 0) {
     s_mfma(sa, kst[0]);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
     m_run = Kn::tile_max(sa, scale_log2);
@@ -426,26 +432,23 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   // Four unrolled iterations per trip, each guarded; the last tile's
   // iteration also computes S of the tile after it on a stale stage, which
   // the mask turns entirely into -inf (no effect on the result).
-  if (wave_active) {
-    for (int j = 0; j < kend; j += 4) {
-      iteration(I0{}, j, sa, sb);
-      if (j + 1 >= kend) break;
-      iteration(I1{}, j + 1, sb, sa);
-      if (j + 2 >= kend) break;
-      iteration(I2{}, j + 2, sa, sb);
-      if (j + 3 >= kend) break;
-      iteration(I3{}, j + 3, sb, sa);
-    }
-  } else {
-    // a wave whose rows all lie past the tile: the same barriers and DMA as
-    // the loop above, none of its arithmetic
-    for (int j = 0; j < kend; ++j) {
-      lds_barrier();
-      const int sk = j % NS, sv = (j + NS - 1) % NS;
-      ld_k(j + NS, sk == 0 ? kst[0] : sk == 1 ? kst[1] : sk == 2 ? kst[2] : kst[3]);
-      ld_v(j + NS - 1, sv == 0 ? vst[0] : sv == 1 ? vst[1] : sv == 2 ? vst[2] : vst[3]);
-      wait_vmcnt<2 * Cfg::DMA_MIN>();
-    }
+  for (int j = 0; j < wkend; j += 4) {
+    iteration(I0{}, j, sa, sb);
+    if (j + 1 >= wkend) break;
+    iteration(I1{}, j + 1, sb, sa);
+    if (j + 2 >= wkend) break;
+    iteration(I2{}, j + 2, sa, sb);
+    if (j + 3 >= wkend) break;
+    iteration(I3{}, j + 3, sb, sa);
+  }
+  // the rest of the item's tiles: the same barriers and DMA as an iteration
+  // above, none of its arithmetic
+  for (int j = wkend; j < kend; ++j) {
+    lds_barrier();
+    const int sk = j % NS, sv = (j + NS - 1) % NS;
+    ld_k(j + NS, sk == 0 ? kst[0] : sk == 1 ? kst[1] : sk == 2 ? kst[2] : kst[3]);
+    ld_v(j + NS - 1, sv == 0 ? vst[0] : sv == 1 ? vst[1] : sv == 2 ? vst[2] : vst[3]);
+    wait_vmcnt<2 * Cfg::DMA_MIN>();
   }
 
   // the loads of the last iterations (tiles past kend) must land before the
