@@ -318,7 +318,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   const int wkend =
       wave_active ? min(kend, __builtin_amdgcn_readfirstlane((slim[min(wrow0 + 31, qend - 1)] + BN - 1) / BN)) : 0;
 
-  // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1 | K3 V2
+  // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1
   // (tile t's resource starts at key row t * BN and ends with the sequence)
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;
