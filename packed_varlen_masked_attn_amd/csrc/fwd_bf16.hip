@@ -51,7 +51,7 @@ struct Bf16Cfg {
   static constexpr int C = D / 8;          // 16-byte chunks per K/V row
   static constexpr int NKC = D / 16;       // MFMA k-steps over the head dimension for S^T
   static constexpr int NDB = D / 32;       // 32-row blocks of O^T
-  static constexpr int NS = 3;             // LDS stages per tensor
+  static constexpr int NS = kBf16Stages;   // LDS stages per tensor
   // K and V tiles are stored unpadded (C 16-byte chunks per row), with the
   // chunks of each row XOR-permuted so that the MFMA operand reads are free of
   // LDS bank conflicts:
@@ -290,7 +290,8 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   const int64_t rs = int64_t(H) * D;  // elements between consecutive tokens of one head
   const uint32_t rs2 = uint32_t(rs) * 2u;  // bytes (the planner keeps L * rs2 below 2^31)
   // bytes from a head's first row of the sequence to the end of its last row
-  const uint32_t head_bytes = uint32_t(L - 1) * rs2 + 2u * D;
+  // (none for a key chunk that holds no rows of this sequence)
+  const uint32_t head_bytes = head_span_bytes(L, rs2, 2u * D);
   constexpr bool paged = PAGED;
   const int32_t kseq = paged ? 0 : cu[it.seq];  // first K/V token of the sequence (contiguous K/V)
   const int64_t base = int64_t(kseq) * rs + int64_t(it.head) * D;
@@ -344,15 +345,14 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
       blk = min(max(blk, 0), pg.num_blocks - 1);
       const int row = k0 & ((1 << pg.block_shift) - 1);
       // the rows of the sequence in this tile; none for a tile past its end
-      // (rs2 >= 2 D makes the expression negative there; the scalar read
-      // keeps the range in scalar registers)
-      bytes = uint32_t(__builtin_amdgcn_readfirstlane(max(min(BN, L - k0) * int(rs2) - int(rs2) + 2 * D, 0)));
+      // (the scalar read keeps the range in scalar registers)
+      bytes = uint32_t(__builtin_amdgcn_readfirstlane(head_span_bytes(min(BN, L - k0), rs2, 2u * D)));
       return reinterpret_cast<const uint8_t*>(contiguous + ((int64_t(blk) << pg.block_shift) + row) * rs +
                                               int64_t(it.head) * D);
     } else {
       const uint32_t o = uint32_t(k0) * rs2;
       // nothing for a tile past the sequence end
-      bytes = head_bytes - uint32_t(__builtin_amdgcn_readfirstlane(min(o, head_bytes)));
+      bytes = uint32_t(__builtin_amdgcn_readfirstlane(tile_range_bytes(head_bytes, o)));
       return reinterpret_cast<const uint8_t*>(contiguous + base) + o;
     }
   };

@@ -144,7 +144,8 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
   std::vector<std::vector<WorkItem>> seq_tiles(nseq);
   for (int32_t s = 0; s < nseq; ++s) {
     const int32_t L = p.seq_len[s], qs = p.q_start[s];
-    const int32_t* qlim = p.key_lim.data() + p.cu_seqlens_q[s] - qs;  // indexed by row of the sequence
+    // key limit of row `row` of the sequence (a queried row, row >= qs)
+    auto qlim = [&](int32_t row) { return p.key_lim[size_t(p.cu_seqlens_q[s]) + size_t(row - qs)]; };
     for (int32_t qa = qs; qa < L; qa += BM) {
       const int32_t qb = std::min(qa + BM, L);
       WorkItem w;
@@ -152,8 +153,8 @@ int plan_sequences(const std::vector<SeqSpec>& seqs, int32_t num_heads, int32_t 
       w.head = 0;
       w.q0 = qa;
       w.q_rows = qb - qa;
-      w.k_full_end = qlim[qa] / BN;
-      w.k_end = (qlim[qb - 1] + BN - 1) / BN;
+      w.k_full_end = qlim(qa) / BN;
+      w.k_end = (qlim(qb - 1) + BN - 1) / BN;
       w.qo_row = p.cu_seqlens_q[s] + (qa - qs);
       w.seq_len = p.kv_len[s];
       seq_tiles[s].push_back(w);

@@ -41,6 +41,27 @@ static_assert(sizeof(WorkItem) == 32, "work item is 8 int32");
 constexpr int32_t kBf16BlockM = PVA_BF16_BM;
 constexpr int32_t kBf16BlockN = PVA_BF16_BN;
 
+// LDS ring depth of each kernel: a work item with k_end key tiles loads the K
+// rows of tiles [0, k_end + stages) and the V rows of tiles
+// [0, k_end + stages - 1) (the loads run ahead of the arithmetic on every
+// path; tiles past the sequence end have an empty range, below).
+constexpr int32_t kBf16Stages = 3;
+constexpr int32_t kFp8Stages = 4;
+
+// Byte ranges of the K/V tile loads. One head's rows of a sequence (or of
+// its key chunk) are `rows` rows, `row_stride` bytes apart and `row_bytes`
+// long; its span runs from the first byte of the first row to the last byte
+// of the last row, and is empty when the sequence holds no key rows.
+PVA_HOST_DEVICE constexpr uint32_t head_span_bytes(int32_t rows, uint32_t row_stride, uint32_t row_bytes) {
+  return rows > 0 ? uint32_t(rows - 1) * row_stride + row_bytes : 0u;
+}
+// A tile's loads go through a buffer resource that starts `tile_offset`
+// bytes into the span and ends with it, so loads at or past the range read
+// zeros without touching memory; a tile past the end gets an empty range.
+PVA_HOST_DEVICE constexpr uint32_t tile_range_bytes(uint32_t span, uint32_t tile_offset) {
+  return span - (tile_offset < span ? tile_offset : span);
+}
+
 // Tile shape used by the kernels for a given element type and head size.
 struct TileShape {
   int32_t bm;  // query rows per work item

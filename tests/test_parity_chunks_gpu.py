@@ -273,3 +273,34 @@ def test_fp8_chunked_partials_and_merge(seed):
     assert mx <= FP8_MAX_ABS
     _, full_l = oracle.chunk_attention(qn, kn, vn, seqs, [0] * len(seqs), [s.length for s in seqs], 1 / math.sqrt(D))
     assert np.max(np.abs(lse_out.cpu().numpy() - full_l)) <= FP8_LSE_MAX_ABS
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_empty_chunk_on_last_sequence(dtype):
+    """A key chunk that holds no row of the last sequence (k_lo = k_hi = L):
+    the K and V tensors end with the previous sequence's chunk rows, the last
+    sequence's work items have an empty K/V span (their tile loads read
+    nothing) and give exactly O = 0 and lse = -inf; the other sequences'
+    partials are unaffected."""
+    seqs = [oracle.make_seq([40, 200], [oracle.CAUSAL, oracle.FULL]),
+            oracle.make_seq([70, 130], [oracle.CAUSAL, oracle.FULL]),
+            oracle.make_seq([33, 100], [oracle.CAUSAL, oracle.FULL])]
+    H, D = 2, 128
+    lo = [0, 50, seqs[2].length]
+    hi = [seqs[0].length, 180, seqs[2].length]
+    if dtype == "bf16":
+        qc, kc, vc = _inputs(seqs, H, D, 131)
+        o, lse = _partial(seqs, qc, kc, vc, lo, hi, H, D)
+        ref_o, ref_l = oracle.chunk_attention(f64(qc), f64(_chunk_rows(kc, seqs, lo, hi)),
+                                              f64(_chunk_rows(vc, seqs, lo, hi)), seqs, lo, hi, 1 / math.sqrt(D))
+        mx = _check_partial(o, lse, ref_o, ref_l)
+    else:
+        codes, scales, (qn, kn, vn) = _fp8_case(seqs, H, D, 132)
+        o, lse = _partial_fp8(seqs, codes, scales, lo, hi, H, D)
+        ref_o, ref_l = oracle.chunk_attention(qn, _chunk_rows(kn, seqs, lo, hi), _chunk_rows(vn, seqs, lo, hi),
+                                              seqs, lo, hi, 1 / math.sqrt(D))
+        mx, _ = _check_partial_fp8(o, lse, ref_o, ref_l)
+    last = slice(seqs[0].q_rows + seqs[1].q_rows, None)
+    assert np.isneginf(lse.cpu().numpy()[last]).all()
+    assert np.all(o.cpu().numpy()[last] == 0.0)
+    say(f"[chunks] {dtype} empty last chunk: O max {mx:.3e}")
