@@ -491,14 +491,18 @@ def main():
     if args.paged:
         print(json.dumps(result), flush=True)
         return
+    padded_out = None
     if not args.no_padded and not is_fp8 and not segmented:
-        result["padded_sdpa"] = padded_baseline(w, q, k, v, scale, args.padded_steps, flops, ms_per_step)
+        result["padded_sdpa"], padded_out = padded_baseline(w, q, k, v, scale, args.padded_steps, flops, ms_per_step)
     torch.cuda.synchronize()
 
     # ---------------- CPU oracle on a bounded sample of the same workload
+    # (it also checks the padded baseline's valid rows on the same slices)
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(w, q, k, v, out, scale, args.cpu_seconds, is_fp8,
-                                              (qs, ks, vs) if is_fp8 else None)
+                                              (qs, ks, vs) if is_fp8 else None, padded_out)
+        if padded_out is not None:
+            result["padded_sdpa"]["vs_oracle_on_sample"] = result["cpu_baseline"].pop("padded_vs_oracle_on_sample")
     print(json.dumps(result), flush=True)
 
 
@@ -590,11 +594,12 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     }), flush=True)
 
 
-def padded_baseline(w, q, k, v, scale, steps, flops, packed_ms):
-    """PyTorch SDPA on the padded batch with the materialised bool mask (the
-    layout the packed path replaces)."""
+def padded_batch(w, q, k, v):
+    """The layout the packed path replaces: every sequence right-padded to
+    Lmax as (B, H, Lmax, D) tensors and a (B, 1, Lmax, Lmax) bool mask that
+    holds each sequence's mixed mask in its top-left L x L block and False
+    elsewhere. Returns (qp, kp, vp, mask, pad_ms, mask_ms)."""
     import torch
-    import torch.nn.functional as F
     dev = q.device
     B, Lmax, H, D = w.nseq, max(w.seq_len), w.num_heads, w.head_dim
     off = np.cumsum([0] + list(w.seq_len))
@@ -617,22 +622,47 @@ def padded_baseline(w, q, k, v, scale, steps, flops, packed_ms):
         mask[s, 0, :L, :L] = causal | img
     torch.cuda.synchronize()
     mask_ms = (time.perf_counter() - t0) * 1e3
+    return qp, kp, vp, mask, pad_ms, mask_ms
 
-    def run():
+
+def padded_sdpa(qp, kp, vp, mask, scale):
+    """torch's scaled_dot_product_attention on the padded batch with the
+    explicit bool mask, limited to its fused kernels (its unfused path would
+    run batched bf16 products on transposed views)."""
+    import torch.nn.functional as F
+    from torch.nn.attention import SDPBackend, sdpa_kernel
+    with sdpa_kernel([SDPBackend.EFFICIENT_ATTENTION, SDPBackend.FLASH_ATTENTION]):
         return F.scaled_dot_product_attention(qp, kp, vp, attn_mask=mask, scale=scale)
 
-    o = run()
+
+def unpad(o, w):
+    """The valid rows of a padded (B, H, Lmax, D) result in the packed
+    [N, H, D] layout (padding rows, whose mask rows are all False, dropped)."""
+    import torch
+    return torch.cat([o[s, :, :L].transpose(0, 1) for s, L in enumerate(w.seq_len)], 0)
+
+
+def padded_baseline(w, q, k, v, scale, steps, flops, packed_ms):
+    """PyTorch SDPA on the padded batch with the materialised bool mask (the
+    layout the packed path replaces), timed as the packed kernel is. Returns
+    the timing record and the valid rows of its result (packed layout, host
+    memory) for the oracle comparison of the CPU leg."""
+    import torch
+    B, Lmax, H, D = w.nseq, max(w.seq_len), w.num_heads, w.head_dim
+    qp, kp, vp, mask, pad_ms, mask_ms = padded_batch(w, q, k, v)
+
+    o = padded_sdpa(qp, kp, vp, mask, scale)
     torch.cuda.synchronize()
     ts = []
     for _ in range(max(1, steps)):
         s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         s.record()
-        o = run()
+        o = padded_sdpa(qp, kp, vp, mask, scale)
         e.record()
         e.synchronize()
         ts.append(s.elapsed_time(e))
     med = statistics.median(ts)
-    # valid rows of the padded result against the packed kernel's output on a few rows (sanity only)
+    valid = unpad(o, w).cpu()
     log(f"[bench] padded SDPA median {med:.3f} ms (pad {pad_ms:.1f} ms, mask {mask_ms:.1f} ms)")
     res = {
         "median_ms": round(med, 4),
@@ -645,12 +675,14 @@ def padded_baseline(w, q, k, v, scale, steps, flops, packed_ms):
     }
     del qp, kp, vp, mask, o
     torch.cuda.empty_cache()
-    return res
+    return res, valid
 
 
-def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales):
+def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales, padded_out=None):
     """The oracle, as it stands, on (sequence, head) slices of the same workload
-    until the time budget is spent; GFLOP/s over the useful FLOPs covered."""
+    until the time budget is spent; GFLOP/s over the useful FLOPs covered. The
+    GPU result is compared with it on those slices, and so are the valid rows
+    of the padded baseline's result when given (packed layout, host memory)."""
     import torch
     import oracle
     try:
@@ -668,6 +700,8 @@ def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales):
     else:
         qn, kn, vn = (x.float().numpy() for x in (qn, kn, vn))
     got = out.float().cpu().numpy()
+    pad_got = padded_out.float().numpy() if padded_out is not None else None
+    pworst, ptotal = 0.0, 0.0
     koff = oracle.offsets(w.seq_len)
     qoff = oracle.offsets(q_rows)
     # a fixed order over (sequence, head): every sequence, head 0 first, then head 1, ...
@@ -693,12 +727,16 @@ def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales):
         worst = max(worst, float(d.max()))
         total += float(d.sum())
         cnt += d.size
+        if pad_got is not None:
+            pd = np.abs(pad_got[qa:qb, h].astype(np.float64) - ref)
+            pworst = max(pworst, float(pd.max()))
+            ptotal += float(pd.sum())
         if t_used >= budget_s:
             break
     tflops = done_flops / t_used / 1e12
     log(f"[bench] CPU oracle: {n} (seq, head) slices in {t_used:.1f}s -> {tflops * 1e3:.2f} GFLOP/s "
         f"on {threads} threads; GPU vs oracle on them: max {worst:.3e} mean {total / max(cnt, 1):.3e}")
-    return {
+    res = {
         "value": round(tflops, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
@@ -708,6 +746,11 @@ def cpu_baseline(w, q, k, v, out, scale, budget_s, is_fp8, fp8_scales):
         "host_cpus_visible": len(os.sched_getaffinity(0)),
         "gpu_vs_oracle_on_sample": {"max_abs": worst, "mean_abs": total / max(cnt, 1)},
     }
+    if pad_got is not None:
+        log(f"[bench] padded SDPA vs oracle on the same slices: max {pworst:.3e} mean {ptotal / max(cnt, 1):.3e}")
+        res["padded_vs_oracle_on_sample"] = {"max_abs": pworst, "mean_abs": ptotal / max(cnt, 1),
+                                             "slices": n}
+    return res
 
 
 if __name__ == "__main__":
