@@ -14,9 +14,8 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# PVA_LIBRARY may name another build of the same library (e.g. a variant
-# compiled with different tile constants); the default is the in-tree build.
-LIB_PATH = os.environ.get("PVA_LIBRARY") or os.path.join(_PKG, "libpva.so")
+# the in-tree build (python -m packed_varlen_masked_attn_amd.build)
+LIB_PATH = os.path.join(_PKG, "libpva.so")
 
 PVA_OK = 0
 PVA_ERR_INVALID_ARG = -1
