@@ -26,8 +26,10 @@
 //                           operand is all ones accumulates l = sum of the
 //                           quantised probabilities, i.e. exactly the weights
 //                           PV applied, so every output row is a convex
-//                           combination of V rows (this keeps early causal
-//                           text rows, which have few keys, accurate).
+//                           combination of V rows.
+//   a tile in which some row's largest probability may carry a sizeable
+//   share of that row's weight (kResidualFactor below) gets a second PV pass
+//   with the probabilities' E4M3 residuals.
 //   O = O^T * v_s / l at the end.
 // The software pipeline (LDS DMA rings, S(j+1) MFMAs beside the exponentials
 // of tile j, PV(j) MFMAs beside the row max of tile j+1) is the bf16
@@ -46,14 +48,27 @@ typedef int i32x2 __attribute__((ext_vector_type(2)));
 // row's reference max (log2 units), which is raised whenever a tile's max
 // exceeds it by more than kP8Lazy. So p stays at or below 2^8.75 < 448
 // (E4M3's largest finite value), and a row's largest p is at least
-// 2^kP8Shift: keys up to 10 log2 units below the row max keep E4M3's normal
+// 2^kP8Shift: keys up to 11 log2 units below the row max keep E4M3's normal
 // range (2^-6 and up, 2^-4 relative rounding) instead of 6 with p_max = 1;
 // below it the spacing is a fixed 2^-9, a large relative error on
-// probabilities that still carry mass when the scores spread widely. The
+// probabilities that still carry mass when the scores spread widely (the
+// bulk of a long row's weight sits there at softmax scales around 0.2). The
 // shift cancels in O / l.
-constexpr float kP8Shift = 4.0f;
-constexpr float kP8Lazy = 4.75f;
+constexpr float kP8Shift = 5.0f;
+constexpr float kP8Lazy = 3.75f;
 static_assert(kP8Shift + kP8Lazy < 8.807f, "largest probability below 448");
+
+// A tile gets a second PV pass with the E4M3 residuals of its probabilities
+// (lo = q(p - q(p)), which carries each weight to about 2^-8 relative
+// instead of 2^-4) when, for some row of the wave, the tile's largest
+// probability exceeds 1/kResidualFactor of the row's sum of weights so far,
+// this tile included. That sum never exceeds the row's final sum, so every
+// key whose final weight reaches 1/kResidualFactor is carried at the finer
+// precision; a key left at E4M3 precision moves its row's output by less
+// than 2^-4 / kResidualFactor times its |v - o|, and such keys' rounding
+// errors are independent. Rows whose weight sits on a few keys (peaked
+// softmax, early causal text rows) are the ones that trigger it.
+constexpr float kResidualFactor = 8.0f;
 
 struct Fp8Cfg {
   static constexpr int D = 128;
@@ -62,7 +77,7 @@ struct Fp8Cfg {
   static constexpr int C = D / 16;     // 16-byte chunks per K/V row
   static constexpr int NKS = D / 64;   // 64-wide MFMA steps over d for S^T
   static constexpr int NDB = D / 32;   // 32-row blocks of O^T (plus one block for l)
-  static constexpr int NS = 4;         // LDS stages per tensor
+  static constexpr int NS = kFp8Stages;  // LDS stages per tensor
   // K and V rows unpadded (C 16-byte chunks each). K's chunks are
   // XOR-permuted per row: the 16-byte operand reads of 16 consecutive rows
   // at one logical chunk then touch 16 different 16-byte bank groups (rows
@@ -153,12 +168,15 @@ struct Fp8Kernel {
       }
   }
 
+  // (IEEE maximum: no canonicalisation of the MFMA results it reads)
+  static __device__ __forceinline__ float max3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+  }
   static __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB], float scale_log2) {
-    float mx = s[0][0];
+    float mx = max3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
-    for (int b = 0; b < NB; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[b][i]);
+    for (int idx = 3; idx + 1 < NB * 16; idx += 2) mx = max3(mx, s[idx / 16][idx % 16], s[(idx + 1) / 16][(idx + 1) % 16]);
+    mx = __builtin_elementwise_maximum(mx, s[NB - 1][15]);
     return half_swap_max(mx) * scale_log2;
   }
 
@@ -173,7 +191,8 @@ struct Fp8Kernel {
   // the probabilities of tile j (program-order interleave, bounded registers)
   static __device__ __forceinline__ void s_with_probs(f32x16 (&snext)[NB], const uint8_t* kst,
                                                       const i32x8 (&qf)[NKS], const f32x16 (&scur)[NB],
-                                                      float scale_log2, float m, i32x8& pb, const KAddr& kad) {
+                                                      float scale_log2, float m, i32x8& pb, float (&pf)[NB * 16],
+                                                      const KAddr& kad) {
     constexpr int NSTEP = NB * NKS;  // (b, c) pairs
     constexpr int WPS = 8 / NSTEP;   // packed probability dwords per MFMA step
     i32x8 ka = read_k(kst, 0, 0, kad);
@@ -188,26 +207,28 @@ struct Fp8Kernel {
 #pragma unroll
       for (int ww = 0; ww < WPS; ++ww) {
         const int w = st * WPS + ww, pbb = w / 4, i0 = 4 * (w % 4);
-        const float p0 = fast_exp2(fmaf(scur[pbb][i0 + 0], scale_log2, -m));
-        const float p1 = fast_exp2(fmaf(scur[pbb][i0 + 1], scale_log2, -m));
-        const float p2 = fast_exp2(fmaf(scur[pbb][i0 + 2], scale_log2, -m));
-        const float p3 = fast_exp2(fmaf(scur[pbb][i0 + 3], scale_log2, -m));
-        pb[w] = pack2<true>(p2, p3, pack2<false>(p0, p1, 0));
+        float* p = pf + 4 * w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(scur[pbb][i0 + e], scale_log2, -m));
+        pb[w] = pack2<true>(p[2], p[3], pack2<false>(p[0], p[1], 0));
       }
       if (st + 1 < NSTEP) ka = kn;
     }
     pin(pb);
   }
 
-  // PV(j) MFMAs (NDB column blocks + the ones block), one V^T operand read
-  // ahead, each followed by a slice of the row max of tile j+1
+  // PV(j) MFMAs (the ones block first, so that the row sum is complete early,
+  // then the NDB column blocks), one V^T operand read ahead, each followed by
+  // a slice of the row max of tile j+1
   static __device__ __forceinline__ float pv_with_max(f32x16 (&o)[NDB + 1], const uint8_t* vst, const i32x8& pb,
                                                       const i32x8& ones, const f32x16 (&snext)[NB],
                                                       float scale_log2, const int (&vrow0)[1], int vsw, int half,
                                                       int p8) {
-    constexpr int PER = (NB * 16 + NDB - 1) / NDB;  // max operations per PV step
-    float mx = snext[0][0];
+    constexpr int NMAX = (NB * 16 - 2) / 2;  // max3 operations over the tile's 32 scores (after the first)
+    constexpr int PER = (NMAX + NDB - 1) / NDB;
+    float mx = max3(snext[0][0], snext[0][1], snext[0][2]);
     i32x8 va = read_v(vst, 0, vrow0, vsw, half, p8);
+    o[NDB] = mfma_fp8(ones, pb, o[NDB]);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       i32x8 vn;
@@ -215,32 +236,31 @@ struct Fp8Kernel {
       o[db] = mfma_fp8(va, pb, o[db]);
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
-        const int idx = db * PER + e;
-        if (idx < NB * 16) mx = fmaxf(mx, snext[idx / 16][idx % 16]);
+        const int t = db * PER + e;  // scores 3 + 2 t and 4 + 2 t
+        if (t < NMAX) {
+          const int a = 3 + 2 * t, b = a + 1;
+          mx = b < NB * 16 ? max3(mx, snext[a / 16][a % 16], snext[b / 16][b % 16])
+                           : __builtin_elementwise_maximum(mx, snext[a / 16][a % 16]);
+        }
       }
       if (db + 1 < NDB) va = vn;
     }
-    o[NDB] = mfma_fp8(ones, pb, o[NDB]);
     return half_swap_max(mx) * scale_log2;
   }
 
-  // second PV pass with the E4M3 residuals of a tile's probabilities
+  // second PV pass with the E4M3 residuals of a tile's probabilities (the
+  // fp32 probabilities pf, minus their E4M3 values pb)
   static __device__ __forceinline__ void pv_residual(f32x16 (&o)[NDB + 1], const uint8_t* vst,
-                                                     const f32x16 (&s)[NB], float scale_log2, float m,
-                                                     const i32x8& pb, const i32x8& ones, const int (&vrow0)[1],
-                                                     int vsw, int half, int p8) {
+                                                     const float (&pf)[NB * 16], const i32x8& pb, const i32x8& ones,
+                                                     const int (&vrow0)[1], int vsw, int half, int p8) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     i32x8 pl;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-      const int b = w / 4, i0 = 4 * (w % 4);
       const f32x2 h01 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], false);
       const f32x2 h23 = __builtin_amdgcn_cvt_pk_f32_fp8(pb[w], true);
-      const float p0 = fast_exp2(fmaf(s[b][i0 + 0], scale_log2, -m)) - h01[0];
-      const float p1 = fast_exp2(fmaf(s[b][i0 + 1], scale_log2, -m)) - h01[1];
-      const float p2 = fast_exp2(fmaf(s[b][i0 + 2], scale_log2, -m)) - h23[0];
-      const float p3 = fast_exp2(fmaf(s[b][i0 + 3], scale_log2, -m)) - h23[1];
-      pl[w] = pack2<true>(p2, p3, pack2<false>(p0, p1, 0));
+      const float* p = pf + 4 * w;
+      pl[w] = pack2<true>(p[2] - h23[0], p[3] - h23[1], pack2<false>(p[0] - h01[0], p[1] - h01[1], 0));
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8(read_v(vst, db, vrow0, vsw, half, p8), pl, o[db]);
@@ -285,7 +305,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const int64_t rs = int64_t(H) * D;  // bytes (one byte per element) between tokens of one head
   const uint32_t rs32 = uint32_t(rs);  // the planner keeps L * rs below 2^31
   // bytes from a head's first row of the sequence to the end of its last row
-  const uint32_t head_bytes = uint32_t(L - 1) * rs32 + uint32_t(D);
+  // (none for a key chunk that holds no rows of this sequence)
+  const uint32_t head_bytes = head_span_bytes(L, rs32, uint32_t(D));
   const int32_t kseq = cu[it.seq];  // first K/V token of the sequence
   const int64_t base = int64_t(kseq) * rs + int64_t(it.head) * D;
   // Q and O hold the queried rows only: row r of the sequence is row qo_row + r - q0
@@ -323,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   vld.init(rs32, lane, wave);
   // (a tile past the sequence end gets an empty range: it reads as zeros and
   // touches no memory; the scalar read keeps the range in scalar registers)
-  auto tile_bytes = [&](uint32_t o) { return head_bytes - uint32_t(__builtin_amdgcn_readfirstlane(min(o, head_bytes))); };
+  auto tile_bytes = [&](uint32_t o) { return uint32_t(__builtin_amdgcn_readfirstlane(tile_range_bytes(head_bytes, o))); };
   auto ld_k = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs32;
     kld.load(make_rsrc(Kb + o, tile_bytes(o)), stage, wave);
@@ -387,12 +408,13 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   };
 
   f32x16 sa[NB], sb[NB];
+  float tmax = -INFINITY;  // the current tile's row max (log2 units)
   if (wkend > 0) {
     s_mfma(sa, kst[0]);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
-    m_run = Kn::tile_max(sa, scale_log2);
+    tmax = Kn::tile_max(sa, scale_log2);
     // a row with no key in range keeps a finite reference (its p are all 0)
-    if (m_run == -INFINITY) m_run = 0.0f;
+    m_run = tmax == -INFINITY ? 0.0f : tmax;
   }
 
   auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[NB], f32x16(&snext)[NB]) {
@@ -403,16 +425,18 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     const int k1 = (j + 1) * BN;
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
-    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run - kP8Shift, pb, kad);
+    float pf[NB * 16];
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run - kP8Shift, pb, pf, kad);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
     const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, scale_log2, vrow0, vsw, half, p8);
-    // A tile the mask cuts for this wave (where rows with few keys live, e.g.
-    // early causal text rows) also gets the E4M3 residual of each probability,
-    // lo = q(p - hi), through a second PV pass: hi + lo carries p to about
-    // 2^-8 relative instead of 2^-4. S(j) is still live here.
-    if (__builtin_expect(k1 > wlim_min, 0))
-      Kn::pv_residual(oacc, vst[SJ], scur, scale_log2, m_run - kP8Shift, pb, ones, vrow0, vsw, half, p8);
+    // residual pass when a key of this tile may carry 1/kResidualFactor of
+    // its row's weight (tile max against the row's sum so far, this tile
+    // included; a row without keys has 0 against 0 and never asks for it)
+    const float pmax = fast_exp2(tmax - m_run + kP8Shift);
+    if (__builtin_expect(wave_any(pmax * kResidualFactor > oacc[NDB][0]), 0))
+      Kn::pv_residual(oacc, vst[SJ], pf, pb, ones, vrow0, vsw, half, p8);
+    tmax = mt;
     const bool need = mt > m_run + kP8Lazy;
     if (__builtin_expect(wave_any(need), 0)) {
       const float alpha = need ? fast_exp2(m_run - mt) : 1.0f;
