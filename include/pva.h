@@ -33,8 +33,9 @@
  *
  * Ownership: the caller owns every tensor and every stream. The library owns
  * only a pva_seg_desc (host copy + device work list), freed by
- * pva_seg_desc_free. No call allocates device memory except
- * pva_seg_desc_build.
+ * pva_seg_desc_free. No call allocates device memory except the descriptor
+ * builders that upload a work list (pva_seg_desc_build, _build_segments,
+ * _build_kv_chunk); pva_seg_desc_build_noalloc uses a fixed buffer instead.
  *
  * Errors: every entry point returns a pva_status (0 on success). Arguments
  * are validated on the host before any launch; nothing throws or aborts
@@ -100,6 +101,36 @@ typedef struct pva_seg_desc pva_seg_desc;
 int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_t nseq,
                        int32_t num_heads, int32_t head_dim, pva_dtype dtype, void* stream,
                        pva_seg_desc** out);
+
+/*
+ * Allocation-free variant of pva_seg_desc_build, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, planning and result, but
+ * the descriptor's device work list and per-row key limits are copied into
+ * a fixed buffer the library holds on each device
+ * (PVA_NOALLOC_SCRATCH_BYTES bytes, kept until the process ends) instead
+ * of a hipMalloc'ed one: no device memory is allocated or freed by this call
+ * or by pva_seg_desc_free of its result (the host-side descriptor itself is
+ * ordinary host memory).
+ *   Size limit: round_up(32 * work items, 256) + 4 * packed tokens must not
+ *   exceed PVA_NOALLOC_SCRATCH_BYTES (the mixed-resolution batch of 8
+ *   sequences and 25,072 tokens at 32 heads needs 305 KB); a larger batch
+ *   gets PVA_ERR_INVALID_ARG before anything is copied.
+ *   One buffer per device: each call replaces the work list of the previous
+ *   no-alloc descriptor of the current device. Forward calls with that older
+ *   descriptor are refused on the host with PVA_ERR_INVALID_ARG (rebuild
+ *   it); descriptors from pva_seg_desc_build are not affected.
+ *   Calls that overlap on one device race: a build that runs while a launch
+ *   with the previous no-alloc descriptor of that device still executes on
+ *   another stream changes the work list under it. Order them on one stream
+ *   (the copy is issued on `stream`), or synchronise in between.
+ * The upload is synchronised on `stream` before return, as in
+ * pva_seg_desc_build.
+ */
+#define PVA_NOALLOC_SCRATCH_BYTES (4u << 20)
+int pva_seg_desc_build_noalloc(const int32_t* text_len, const int32_t* image_len, int32_t nseq,
+                               int32_t num_heads, int32_t head_dim, pva_dtype dtype, void* stream,
+                               pva_seg_desc** out);
 
 /* Same planning without touching any device: the result can be inspected
  * (accessors below) but not launched. For host-side tests and tools. */

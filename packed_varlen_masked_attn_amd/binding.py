@@ -33,7 +33,7 @@ EXPORTED = [
     "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
     "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
     "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials", "packed_attn_fwd_paged",
-    "packed_attn_fwd_partial_fp8",
+    "packed_attn_fwd_partial_fp8", "pva_seg_desc_build_noalloc",
 ]
 
 
@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
     vp = ctypes.c_void_p
     sig("pva_seg_desc_build", [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
                                      vp, ctypes.POINTER(vp)], ctypes.c_int)
+    sig("pva_seg_desc_build_noalloc", [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int,
+                                       vp, ctypes.POINTER(vp)], ctypes.c_int)
     sig("pva_seg_desc_build_host", [i32p, i32p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                           ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
     sig("pva_seg_desc_build_segments", [i32p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_int32,
@@ -124,11 +126,14 @@ class SegDesc:
     """A planned batch composition (segment descriptors + ordered work list).
 
     Built once per composition and re-used by every launch over it.
-    ``host_only=True`` plans without touching a GPU (for inspection only).
+    ``host_only=True`` plans without touching a GPU (for inspection only);
+    ``noalloc=True`` keeps the device work list in the library's fixed
+    per-device buffer (pva_seg_desc_build_noalloc: no device allocation, and
+    only the latest such descriptor of a device can be launched).
     """
 
     def __init__(self, text_len: Sequence[int], image_len: Sequence[int], num_heads: int, head_dim: int,
-                 dtype: str = "bf16", stream=None, host_only: bool = False):
+                 dtype: str = "bf16", stream=None, host_only: bool = False, noalloc: bool = False):
         if len(text_len) != len(image_len):
             raise PvaError(PVA_ERR_INVALID_ARG, "text_len and image_len differ in length")
         if dtype not in DTYPES:
@@ -137,9 +142,15 @@ class SegDesc:
         t_arr, t_ptr = _i32_array(text_len)
         i_arr, i_ptr = _i32_array(image_len)
         h = ctypes.c_void_p()
+        if host_only and noalloc:
+            raise PvaError(PVA_ERR_INVALID_ARG, "host_only and noalloc exclude each other")
         if host_only:
             st = L.pva_seg_desc_build_host(t_ptr, i_ptr, len(t_arr), int(num_heads), int(head_dim),
                                            DTYPES[dtype], ctypes.byref(h))
+        elif noalloc:
+            st = L.pva_seg_desc_build_noalloc(t_ptr, i_ptr, len(t_arr), int(num_heads), int(head_dim),
+                                              DTYPES[dtype], ctypes.c_void_p(_stream_handle(stream)),
+                                              ctypes.byref(h))
         else:
             st = L.pva_seg_desc_build(t_ptr, i_ptr, len(t_arr), int(num_heads), int(head_dim), DTYPES[dtype],
                                       ctypes.c_void_p(_stream_handle(stream)), ctypes.byref(h))

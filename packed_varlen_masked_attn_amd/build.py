@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpva.so")
 
-SOURCES = ["plan.cpp", "api.cpp", "fwd_bf16.hip", "fwd_fp8.hip", "merge.hip"]
+SOURCES = ["plan.cpp", "api.cpp", "fwd_bf16.hip", "fwd_fp8.hip", "merge.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
@@ -54,7 +54,7 @@ def _compile(src: str, verbose: bool) -> str:
 def build(verbose: bool = False) -> str:
     """Compile every source and link libpva.so next to this file. Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(5, len(SOURCES))) as ex:
+    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
         objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]

@@ -78,13 +78,24 @@ int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu_
   if (dev != d->device)
     return set_error(PVA_ERR_INVALID_ARG, "seg_desc was built on device " + std::to_string(d->device) +
                                               " but the current device is " + std::to_string(dev));
+  if (d->scratch_generation != 0 && !pva::scratch_is_current(d->device, d->scratch_generation))
+    return set_error(PVA_ERR_INVALID_ARG,
+                     "a later pva_seg_desc_build_noalloc on this device replaced this descriptor's work list: "
+                     "build it again");
   return PVA_OK;
 }
 
-// Builds a plan with `plan_fn` and, if asked, uploads the work list and the
-// key limits to the current device (one allocation: items, then limits).
+// Where a descriptor's device work list goes.
+enum class Placement {
+  kHostOnly,       // nowhere: inspection only
+  kOwnAllocation,  // one hipMalloc per descriptor, freed with it
+  kScratch,        // the device's fixed no-alloc buffer (no allocation)
+};
+
+// Builds a plan with `plan_fn` and, unless host-only, uploads the work list
+// and the key limits to the current device (one buffer: items, then limits).
 template <typename PlanFn>
-int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) {
+int build_common(PlanFn plan_fn, Placement placement, void* stream, pva_seg_desc** out) {
   if (!out) return set_error(PVA_ERR_INVALID_ARG, "out is NULL");
   *out = nullptr;
   pva_seg_desc* d = new (std::nothrow) pva_seg_desc();
@@ -101,7 +112,7 @@ int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) 
     delete d;
     return set_error(st, err);
   }
-  if (upload) {
+  if (placement != Placement::kHostOnly) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) {
@@ -112,10 +123,19 @@ int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) 
     const size_t item_bytes = (d->plan.items.size() * sizeof(pva::WorkItem) + 255) / 256 * 256;
     const size_t lim_bytes = d->plan.key_lim.size() * sizeof(int32_t);
     void* base = nullptr;
-    e = hipMalloc(&base, item_bytes + lim_bytes);
-    if (e != hipSuccess) {
-      delete d;
-      return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
+    if (placement == Placement::kScratch) {
+      // the fixed buffer is never allocated or freed here
+      st = pva::scratch_acquire(dev, item_bytes + lim_bytes, &base, &d->scratch_generation, &err);
+      if (st != PVA_OK) {
+        delete d;
+        return set_error(st, err);
+      }
+    } else {
+      e = hipMalloc(&base, item_bytes + lim_bytes);
+      if (e != hipSuccess) {
+        delete d;
+        return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
+      }
     }
     d->d_items = base;
     d->d_lims = reinterpret_cast<int32_t*>(static_cast<char*>(base) + item_bytes);
@@ -126,7 +146,7 @@ int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) 
     if (e == hipSuccess) e = hipMemcpyAsync(d->d_lims, d->plan.key_lim.data(), lim_bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
-      (void)hipFree(base);
+      if (placement == Placement::kOwnAllocation) (void)hipFree(base);
       delete d;
       return hip_error(e, "uploading the work list");
     }
@@ -136,12 +156,12 @@ int build_common(PlanFn plan_fn, bool upload, void* stream, pva_seg_desc** out) 
 }
 
 int build_two(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads, int32_t head_dim,
-              pva_dtype dtype, bool upload, void* stream, pva_seg_desc** out) {
+              pva_dtype dtype, Placement placement, void* stream, pva_seg_desc** out) {
   return build_common(
       [&](pva::Plan* p, std::string* err) {
         return pva::build_plan(text_len, image_len, nseq, num_heads, head_dim, dtype, p, err);
       },
-      upload, stream, out);
+      placement, stream, out);
 }
 
 int build_segs(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count, const int32_t* q_start,
@@ -152,7 +172,7 @@ int build_segs(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* s
         return pva::build_plan_segments(seg_len, seg_kind, seg_count, q_start, k_lo, k_hi, nseq, num_heads, head_dim,
                                         dtype, p, err);
       },
-      upload, stream, out);
+      upload ? Placement::kOwnAllocation : Placement::kHostOnly, stream, out);
 }
 
 int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
@@ -192,12 +212,17 @@ extern "C" {
 
 int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                        int32_t head_dim, pva_dtype dtype, void* stream, pva_seg_desc** out) {
-  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, true, stream, out);
+  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, Placement::kOwnAllocation, stream, out);
+}
+
+int pva_seg_desc_build_noalloc(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
+                               int32_t head_dim, pva_dtype dtype, void* stream, pva_seg_desc** out) {
+  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, Placement::kScratch, stream, out);
 }
 
 int pva_seg_desc_build_host(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
                             int32_t head_dim, pva_dtype dtype, pva_seg_desc** out) {
-  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, false, nullptr, out);
+  return build_two(text_len, image_len, nseq, num_heads, head_dim, dtype, Placement::kHostOnly, nullptr, out);
 }
 
 int pva_seg_desc_build_segments(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* seg_count,
@@ -270,7 +295,7 @@ int pva_seg_desc_work_items(const pva_seg_desc* d, const int32_t** items, int32_
 
 void pva_seg_desc_free(pva_seg_desc* d) {
   if (!d) return;
-  if (d->d_items) {
+  if (d->d_items && d->scratch_generation == 0) {  // the no-alloc buffer is never freed
     int cur = -1;
     (void)hipGetDevice(&cur);
     if (cur != d->device && d->device >= 0) (void)hipSetDevice(d->device);

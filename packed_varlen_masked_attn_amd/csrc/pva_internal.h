@@ -1,6 +1,7 @@
 // Internal declarations shared by the planner, the C-ABI layer and the kernels.
 #pragma once
 
+#include <cstddef>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -102,6 +103,15 @@ struct PagedKV {
   int32_t num_blocks;    // blocks in each pool
 };
 
+// Fixed device buffer of the allocation-free descriptor builder (one per
+// device). scratch_acquire hands out its address on the current device
+// (taken once per device) for `bytes` bytes and starts a new generation,
+// which retires the previous no-alloc descriptor of that device;
+// scratch_is_current tells whether a descriptor's generation still owns it.
+constexpr size_t kNoAllocScratchBytes = PVA_NOALLOC_SCRATCH_BYTES;
+int scratch_acquire(int device, size_t bytes, void** ptr, uint64_t* generation, std::string* err);
+bool scratch_is_current(int device, uint64_t generation);
+
 // Validates and plans; on failure returns a status and fills `err`.
 // Two segments per sequence: text (causal) then one image block (full).
 int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,
@@ -120,4 +130,5 @@ struct pva_seg_desc {
   void* d_items = nullptr;    // device copy of plan.items (nullptr for host-only descriptors)
   int32_t* d_lims = nullptr;  // device copy of plan.key_lim (same allocation as d_items)
   int32_t device = -1;        // HIP device the work list lives on
+  uint64_t scratch_generation = 0;  // > 0: the work list lives in that device's no-alloc buffer
 };

@@ -40,6 +40,11 @@ int launch_fwd_fp8(const void*, const void*, const void*, const float*, const fl
   std::fprintf(stderr, "FAIL: an fp8 launch was reached\n");
   std::abort();
 }
+int scratch_acquire(int, size_t, void**, uint64_t*, std::string*) {
+  std::fprintf(stderr, "FAIL: the no-alloc buffer was reached\n");
+  std::abort();
+}
+bool scratch_is_current(int, uint64_t) { return false; }
 }  // namespace pva
 
 namespace {
