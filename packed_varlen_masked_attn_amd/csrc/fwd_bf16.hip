@@ -352,7 +352,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
     } else {
       const uint32_t o = uint32_t(k0) * rs2;
       // nothing for a tile past the sequence end
-      bytes = uint32_t(__builtin_amdgcn_readfirstlane(tile_range_bytes(head_bytes, o)));
+      bytes = tile_range_bytes_uniform(head_bytes, o);
       return reinterpret_cast<const uint8_t*>(contiguous + base) + o;
     }
   };

@@ -172,12 +172,13 @@ struct Fp8Kernel {
   static __device__ __forceinline__ float max3(float a, float b, float c) {
     return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
   }
-  static __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB], float scale_log2) {
+  // the row's largest raw score in a tile (shared by both half-waves)
+  static __device__ __forceinline__ float tile_max(const f32x16 (&s)[NB]) {
     float mx = max3(s[0][0], s[0][1], s[0][2]);
 #pragma unroll
     for (int idx = 3; idx + 1 < NB * 16; idx += 2) mx = max3(mx, s[idx / 16][idx % 16], s[(idx + 1) / 16][(idx + 1) % 16]);
     mx = __builtin_elementwise_maximum(mx, s[NB - 1][15]);
-    return half_swap_max(mx) * scale_log2;
+    return half_swap_max(mx);
   }
 
   // E4M3 probabilities of one element pair -> two bytes of a packed dword
@@ -210,7 +211,8 @@ struct Fp8Kernel {
         float* p = pf + 4 * w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) p[e] = fast_exp2(fmaf(scur[pbb][i0 + e], scale_log2, -m));
-        pb[w] = pack2<true>(p[2], p[3], pack2<false>(p[0], p[1], 0));
+        // (both halves of the dword are written: no zero-initialised target)
+        pb[w] = pack2<true>(p[2], p[3], pack2<false>(p[0], p[1], pb[w]));
       }
       if (st + 1 < NSTEP) ka = kn;
     }
@@ -219,16 +221,18 @@ struct Fp8Kernel {
 
   // PV(j) MFMAs (the ones block first, so that the row sum is complete early,
   // then the NDB column blocks), one V^T operand read ahead, each followed by
-  // a slice of the row max of tile j+1
+  // a slice of the row max of tile j+1 (raw scores)
   static __device__ __forceinline__ float pv_with_max(f32x16 (&o)[NDB + 1], const uint8_t* vst, const i32x8& pb,
                                                       const i32x8& ones, const f32x16 (&snext)[NB],
-                                                      float scale_log2, const int (&vrow0)[1], int vsw, int half,
-                                                      int p8) {
+                                                      const int (&vrow0)[1], int vsw, int half, int p8) {
     constexpr int NMAX = (NB * 16 - 2) / 2;  // max3 operations over the tile's 32 scores (after the first)
     constexpr int PER = (NMAX + NDB - 1) / NDB;
     float mx = max3(snext[0][0], snext[0][1], snext[0][2]);
     i32x8 va = read_v(vst, 0, vrow0, vsw, half, p8);
     o[NDB] = mfma_fp8(ones, pb, o[NDB]);
+    // keeps the scheduler from sinking the row-sum MFMA to the end of the
+    // phase, where the residual test would wait for its result
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
       i32x8 vn;
@@ -245,7 +249,7 @@ struct Fp8Kernel {
       }
       if (db + 1 < NDB) va = vn;
     }
-    return half_swap_max(mx) * scale_log2;
+    return half_swap_max(mx);
   }
 
   // second PV pass with the E4M3 residuals of a tile's probabilities (the
@@ -344,7 +348,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   vld.init(rs32, lane, wave);
   // (a tile past the sequence end gets an empty range: it reads as zeros and
   // touches no memory; the scalar read keeps the range in scalar registers)
-  auto tile_bytes = [&](uint32_t o) { return uint32_t(__builtin_amdgcn_readfirstlane(tile_range_bytes(head_bytes, o))); };
+  auto tile_bytes = [&](uint32_t o) { return tile_range_bytes_uniform(head_bytes, o); };
   auto ld_k = [&](int t, uint8_t* stage) {
     const uint32_t o = uint32_t(t * BN) * rs32;
     kld.load(make_rsrc(Kb + o, tile_bytes(o)), stage, wave);
@@ -381,10 +385,25 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   for (int db = 0; db <= NDB; ++db) oacc[db] = f32x16{};
   i32x8 ones;
 #pragma unroll
-  for (int w = 0; w < 8; ++w) ones[w] = 0x38383838;  // E4M3 1.0 in every byte
-  // reference max of the row (log2 units); the probabilities are
-  // p = 2^(score - m_run + kP8Shift), see kP8Shift
-  float m_run = -INFINITY;
+  for (int w = 0; w < 8; ++w) {
+    // E4M3 1.0 in every byte, written by an opaque move: as a known constant
+    // the compiler would re-create the 8-register operand every tile
+    int one4;
+    asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
+    ones[w] = one4;
+  }
+  // The row's reference max m (log2 units) is kept as the derived values the
+  // tile loop uses: the exponent bias mb = m - kP8Shift of the probabilities
+  // p = 2^(score * scale_log2 - mb), the bias of the residual test and the
+  // raw-score threshold past which a tile moves the reference (they change
+  // only when it moves).
+  float m_run = 0.0f, mb = -kP8Shift, mres = 0.0f, thr = 0.0f;
+  auto set_reference = [&](float m) {
+    m_run = m;
+    mb = m - kP8Shift;
+    mres = mb - __builtin_log2f(kResidualFactor);
+    thr = (m + kP8Lazy) / scale_log2;
+  };
 
   // per-lane constant parts of the V^T transpose-read addresses: this lane
   // feeds key row 16 r + vrow0 (r = 0..3), columns 32 db + 16 half + 8 p8
@@ -408,13 +427,13 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   };
 
   f32x16 sa[NB], sb[NB];
-  float tmax = -INFINITY;  // the current tile's row max (log2 units)
+  float tmax = -INFINITY;  // the current tile's largest raw score of the row
   if (wkend > 0) {
     s_mfma(sa, kst[0]);
     if (BN > wlim_min) Kn::mask(sa, 0, g, mylim);
-    tmax = Kn::tile_max(sa, scale_log2);
+    tmax = Kn::tile_max(sa);
     // a row with no key in range keeps a finite reference (its p are all 0)
-    m_run = tmax == -INFINITY ? 0.0f : tmax;
+    set_reference(tmax == -INFINITY ? 0.0f : tmax * scale_log2);
   }
 
   auto iteration = [&](auto sj_tag, int j, f32x16(&scur)[NB], f32x16(&snext)[NB]) {
@@ -426,25 +445,26 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
     float pf[NB * 16];
-    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, m_run - kP8Shift, pb, pf, kad);
+    Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, mb, pb, pf, kad);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
-    const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, scale_log2, vrow0, vsw, half, p8);
+    const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, vrow0, vsw, half, p8);
     // residual pass when a key of this tile may carry 1/kResidualFactor of
-    // its row's weight (tile max against the row's sum so far, this tile
-    // included; a row without keys has 0 against 0 and never asks for it)
-    const float pmax = fast_exp2(tmax - m_run + kP8Shift);
-    if (__builtin_expect(wave_any(pmax * kResidualFactor > oacc[NDB][0]), 0))
+    // its row's weight: kResidualFactor times the tile's largest probability
+    // against the row's sum so far, this tile included (a row without keys
+    // has 0 against 0 and never asks for it)
+    if (__builtin_expect(wave_any(fast_exp2(fmaf(tmax, scale_log2, -mres)) > oacc[NDB][0]), 0))
       Kn::pv_residual(oacc, vst[SJ], pf, pb, ones, vrow0, vsw, half, p8);
     tmax = mt;
-    const bool need = mt > m_run + kP8Lazy;
+    const bool need = mt > thr;
     if (__builtin_expect(wave_any(need), 0)) {
-      const float alpha = need ? fast_exp2(m_run - mt) : 1.0f;
+      const float mtl = mt * scale_log2;
+      const float alpha = need ? fast_exp2(m_run - mtl) : 1.0f;
 #pragma unroll
       for (int db = 0; db <= NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      m_run = need ? mt : m_run;
+      if (need) set_reference(mtl);
     }
     wait_vmcnt<2 * Cfg::DMA_MIN>();
   };
@@ -512,7 +532,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     }
     if (lse && g == 0)
       lse[int64_t(it.qo_row - it.q0 + qrow) * H + it.head] =
-          lt > 0.0f ? 0.6931471805599453f * (m_run - kP8Shift + __log2f(lt)) : -INFINITY;
+          lt > 0.0f ? 0.6931471805599453f * (mb + __log2f(lt)) : -INFINITY;
   }
 }
 

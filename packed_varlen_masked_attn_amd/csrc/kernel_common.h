@@ -54,6 +54,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// tile_range_bytes(span, offset) = span - min(offset, span) for wave-uniform
+// values, on the scalar unit (the compiler forms that saturating subtract on
+// the vector unit and reads it back with v_readfirstlane; here: s_min_u32
+// then s_sub_u32, the same two operations)
+__device__ __forceinline__ uint32_t tile_range_bytes_uniform(uint32_t span, uint32_t offset) {
+  uint32_t r;
+  asm("s_min_u32 %0, %1, %2\n\ts_sub_u32 %0, %2, %0" : "=&s"(r) : "s"(offset), "s"(span) : "scc");
+  return r;
+}
+
 // Per-lane state of the online softmax for one query column.
 struct RowState {
   float m;  // reference max (log2 units); O and l are relative to it
