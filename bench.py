@@ -61,6 +61,10 @@ def parse():
     ap.add_argument("--padded-steps", type=int, default=10)
     ap.add_argument("--no-padded", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="default workload only: skip the kernel timings of the fp8 mixed batch, the 1024^2 pair "
+                         "and the SP4 head share that the line otherwise carries under other_configs")
+    ap.add_argument("--other-steps", type=int, default=50, help="timed launches per other configuration")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget of the CPU oracle sample")
     ap.add_argument("--kernel-only", action="store_true", help="time the kernel only (for profilers)")
     ap.add_argument("--paged", type=int, default=0, metavar="BLOCK",
@@ -491,6 +495,12 @@ def main():
     if args.paged:
         print(json.dumps(result), flush=True)
         return
+    # ---------------- the other configurations of the pages' workloads, kernel only
+    # (own inputs and outputs: the headline's output stays for the oracle leg)
+    if w.name == "mixed_res_cfg_batch" and not args.no_other_configs:
+        result["other_configs"] = {key: config_record(key, args.other_steps, max(5, args.warmup))
+                                   for key in ("mixed_res_fp8", "single_1024", "sp4_share")}
+
     padded_out = None
     if not args.no_padded and not is_fp8 and not segmented:
         result["padded_sdpa"], padded_out = padded_baseline(w, q, k, v, scale, args.padded_steps, flops, ms_per_step)
@@ -504,6 +514,82 @@ def main():
         if padded_out is not None:
             result["padded_sdpa"]["vs_oracle_on_sample"] = result["cpu_baseline"].pop("padded_vs_oracle_on_sample")
     print(json.dumps(result), flush=True)
+
+
+def config_record(key, steps, warmup):
+    """Kernel timing of another workload, taken as the headline's kernel
+    average is: `warmup` launches, then `steps` launches with HIP events on
+    the launch stream. Reports useful TFLOP/s against the kernel's own MFMA
+    peak (and the bf16 one), plus the stored HBM-byte record while the
+    kernel sources match it."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    w = workloads.WORKLOADS[key]()
+    dev = torch.device("cuda:0")
+    is_fp8 = w.dtype == "fp8"
+    dtype = "fp8" if is_fp8 else "bf16"
+    H, D = w.num_heads, w.head_dim
+    scale = 1.0 / math.sqrt(D)
+    t0 = time.time()
+    if is_fp8:
+        q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+        q, k, v = (x.view(torch.uint8).to(dev) for x in (q8, k8, v8))
+        sc = [torch.from_numpy(x).to(dev) for x in (qs, ks, vs)]
+    else:
+        q, k, v = (x.to(dev) for x in workloads.bf16_inputs(w))
+    out = torch.empty((w.total_tokens, H, D), dtype=torch.bfloat16, device=dev)
+    desc = pva.SegDesc(w.text_len, w.image_len, H, D, dtype)
+    cu = torch.from_numpy(desc.cu_seqlens).to(dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        if is_fp8:
+            pva.packed_attn_fwd_fp8(q, k, v, *sc, cu, desc, scale, out, stream)
+        else:
+            pva.packed_attn_fwd(q, k, v, cu, desc, scale, out, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    gc.disable()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    gc.enable()
+    kms = [a.elapsed_time(b) for a, b in zip(starts, ends)]
+    k_avg = statistics.fmean(kms)
+    flops = desc.useful_flops
+    achieved = flops / (k_avg * 1e-3) / 1e12
+    traffic = stored_traffic(dtype, w.name)
+    rec = {
+        "workload": w.name,
+        "text_len": list(w.text_len), "image_len": list(w.image_len), "num_heads": H, "head_dim": D,
+        "dtype": dtype,
+        "useful_flop": flops,
+        "kernel": "fwd_fp8_kernel" if is_fp8 else f"fwd_bf16_kernel<{D}>",
+        "kernel_ms": {"avg": round(k_avg, 5), "median": round(statistics.median(kms), 5),
+                      "p10": round(pct(kms, 10), 5), "p90": round(pct(kms, 90), 5)},
+        "achieved_tflops": round(achieved, 2),
+        "peak": PEAK_TFLOPS[dtype],
+        "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
+        "pct_of_bf16_peak": round(100.0 * achieved / PEAK_TFLOPS["bf16"], 2),
+        "traffic": traffic,
+        "algorithmic_bytes": algorithmic_bytes(w),
+    }
+    if traffic:
+        rec["hbm_gbs"] = round(traffic / (k_avg * 1e-3) / 1e9, 1)
+    ctr = stored_counters(dtype, w.name)
+    if ctr:
+        rec["counters"] = ctr
+    log(f"[bench] {w.name}: kernel avg {k_avg:.4f} ms -> {achieved:.1f} useful TFLOP/s "
+        f"({100 * achieved / PEAK_TFLOPS[dtype]:.1f} % of the {dtype} peak), inputs {time.time() - t0:.1f}s")
+    del q, k, v, out
+    torch.cuda.empty_cache()
+    return rec
 
 
 def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
