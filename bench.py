@@ -696,7 +696,8 @@ def padded_batch(w, q, k, v):
         L = w.seq_len[s]
         for src, dst in ((q, qp), (k, kp), (v, vp)):
             dst[s, :, :L] = src[off[s]:off[s + 1]].transpose(0, 1)
-    torch.cuda.synchronize()
+    if dev.type == "cuda":
+        torch.cuda.synchronize()
     pad_ms = (time.perf_counter() - t0) * 1e3
     t0 = time.perf_counter()
     mask = torch.zeros((B, 1, Lmax, Lmax), dtype=torch.bool, device=dev)
@@ -706,7 +707,8 @@ def padded_batch(w, q, k, v):
         causal = ar[None, :L] <= ar[:L, None]
         img = (ar[:L] >= T)[:, None]
         mask[s, 0, :L, :L] = causal | img
-    torch.cuda.synchronize()
+    if dev.type == "cuda":
+        torch.cuda.synchronize()
     mask_ms = (time.perf_counter() - t0) * 1e3
     return qp, kp, vp, mask, pad_ms, mask_ms
 

@@ -304,12 +304,14 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   // queried row and never decrease along the rows, so the wave's first row
   // has the smallest.
   const int qend = it.q0 + it.q_rows;
-  const int32_t* slim = lims + (it.qo_row - it.q0);
+  // key limit of query row r of the sequence (r in [q0, qend)): stored at
+  // queried-row index qo_row + r - q0
+  auto row_lim = [&](int r) { return lims[it.qo_row + (r - it.q0)]; };
   const int wrow0 = it.q0 + 32 * wave;
   const int qrow = wrow0 + l32;
-  const int mylim = qrow < qend ? slim[qrow] : L;
+  const int mylim = qrow < qend ? row_lim(qrow) : L;
   const bool wave_active = wrow0 < qend;  // uniform per wave: a scalar branch
-  const int wlim_min = wave_active ? slim[wrow0] : L;
+  const int wlim_min = wave_active ? row_lim(wrow0) : L;
   const int kend = it.k_end;
   // The wave's own last key tile: past the key limit of its last row every
   // tile is fully masked for all its rows (limits never decrease along the
@@ -317,7 +319,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   // (in the last tile of a sequence), the wave only moves its share of the
   // K/V tiles and meets the barriers (the loop after the tile loop below).
   const int wkend =
-      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((slim[min(wrow0 + 31, qend - 1)] + BN - 1) / BN)) : 0;
+      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((row_lim(min(wrow0 + 31, qend - 1)) + BN - 1) / BN)) : 0;
 
   // prologue DMA in the order the tiles are needed: K0 K1 V0 | K2 V1
   // (tile t's resource starts at key row t * BN and ends with the sequence)

@@ -326,19 +326,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   // rows held); the limits never decrease along the rows, so the wave's
   // first row has the smallest. The limits are stored per queried row.
   const int qend = it.q0 + it.q_rows;
-  const int32_t* slim = lims + (it.qo_row - it.q0);
+  // key limit of query row r of the sequence (r in [q0, qend)): stored at
+  // queried-row index qo_row + r - q0
+  auto row_lim = [&](int r) { return lims[it.qo_row + (r - it.q0)]; };
   const int qrow = it.q0 + 32 * wave + l32;
-  const int mylim = qrow < qend ? slim[qrow] : L;
+  const int mylim = qrow < qend ? row_lim(qrow) : L;
   const int wrow0 = it.q0 + 32 * wave;
   const bool wave_active = wrow0 < qend;
-  const int wlim_min = wave_active ? slim[wrow0] : L;
+  const int wlim_min = wave_active ? row_lim(wrow0) : L;
   const int kend = it.k_end;
   // the wave's own last key tile (past its last row's key limit every tile is
   // fully masked for all its rows); 0 for a wave whose rows all lie past the
   // tile. From there on the wave only moves its share of the K/V tiles and
   // meets the barriers.
   const int wkend =
-      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((slim[min(wrow0 + 31, qend - 1)] + BN - 1) / BN)) : 0;
+      wave_active ? min(kend, __builtin_amdgcn_readfirstlane((row_lim(min(wrow0 + 31, qend - 1)) + BN - 1) / BN)) : 0;
 
   typename Kn::KLoader kld;
   typename Kn::VLoader vld;

@@ -115,3 +115,20 @@ def test_source_hash_ignores_comments():
     assert bench.code_tokens(code) == bench.code_tokens(code.replace("one", "uno").replace("two", "dos"))
     assert bench.code_tokens(code) != bench.code_tokens(code.replace("x + 1", "x + 2"))
     assert '"a // b"' in bench.code_tokens(code)
+
+
+def test_padded_batch_matches_the_oracle_padding():
+    """The padded comparator's inputs, built by the bench on host tensors:
+    layout and (B, 1, Lmax, Lmax) mask equal the oracle's padded formulation
+    exactly, and unpad() returns the packed rows."""
+    import numpy as np
+    import torch
+    import oracle
+    import workloads
+    w = workloads.custom([37, 0, 200, 5, 1], [300, 64, 0, 0, 3], 2, 64, seed=12, name="padded_host")
+    q, k, v = workloads.bf16_inputs(w)
+    qp, kp, vp, mask, _, _ = bench.padded_batch(w, q, k, v)
+    assert np.array_equal(mask.numpy(), oracle.padded_mask(w.text_len, w.image_len))
+    for x, xp in ((q, qp), (k, kp), (v, vp)):
+        assert np.array_equal(xp.float().numpy().astype(np.float64), oracle.padded_layout(x.float().numpy(), w.seq_len))
+    assert torch.equal(bench.unpad(qp, w), q)
