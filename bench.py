@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mixed_res", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--softmax-scale", type=float, default=None,
+                    help="softmax scale of the timed launches (default 1/sqrt(D)); larger values give peaked rows")
     ap.add_argument("--cold-iters", type=int, default=30, help="launches timed after a cache-evicting write")
     ap.add_argument("--padded-steps", type=int, default=10)
     ap.add_argument("--no-padded", action="store_true")
@@ -317,7 +319,7 @@ def main():
     is_fp8 = w.dtype == "fp8"
     dtype = "fp8" if is_fp8 else "bf16"
     H, D = w.num_heads, w.head_dim
-    scale = 1.0 / math.sqrt(D)
+    scale = 1.0 / math.sqrt(D) if args.softmax_scale is None else args.softmax_scale
     if segmented:
         log(f"[bench] workload {w.name}: {w.nseq} sequences, Nk={w.total_tokens} Nq={w.total_q} H={H} D={D} {dtype}")
     else:
@@ -440,6 +442,7 @@ def main():
             "num_heads": H,
             "head_dim": D,
             "tile": list(desc.tile),
+            "softmax_scale": scale,
             "parallelism": "single GPU",
             **({"paged_block_rows": args.paged} if args.paged else {}),
         },
