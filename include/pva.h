@@ -117,9 +117,10 @@ int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_
  *   sequences and 25,072 tokens at 32 heads needs 305 KB); a larger batch
  *   gets PVA_ERR_INVALID_ARG before anything is copied.
  *   One buffer per device: each call replaces the work list of the previous
- *   no-alloc descriptor of the current device. Forward calls with that older
- *   descriptor are refused on the host with PVA_ERR_INVALID_ARG (rebuild
- *   it); descriptors from pva_seg_desc_build are not affected.
+ *   no-alloc descriptor of the current device (also when its upload then
+ *   fails). Forward calls with that older descriptor are refused on the host
+ *   with PVA_ERR_INVALID_ARG (rebuild it); descriptors from
+ *   pva_seg_desc_build are not affected.
  *   Calls that overlap on one device race: a build that runs while a launch
  *   with the previous no-alloc descriptor of that device still executes on
  *   another stream changes the work list under it. Order them on one stream
