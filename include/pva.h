@@ -124,7 +124,10 @@ int pva_seg_desc_build(const int32_t* text_len, const int32_t* image_len, int32_
  *   Calls that overlap on one device race: a build that runs while a launch
  *   with the previous no-alloc descriptor of that device still executes on
  *   another stream changes the work list under it. Order them on one stream
- *   (the copy is issued on `stream`), or synchronise in between.
+ *   (the copy is issued on `stream`), or synchronise in between. A HIP graph
+ *   that captured launches with a no-alloc descriptor reads the buffer when
+ *   it is replayed (the host-side check does not run then): replay it only
+ *   while that descriptor is still its device's current no-alloc one.
  * The upload is synchronised on `stream` before return, as in
  * pva_seg_desc_build.
  */

@@ -80,3 +80,43 @@ def test_noalloc_rejects_a_batch_past_the_buffer():
         pva.SegDesc([0], [1_500_000], 1, 64, "bf16", noalloc=True)
     assert ei.value.status == pva.PVA_ERR_INVALID_ARG
     assert "PVA_NOALLOC_SCRATCH_BYTES" in str(ei.value)
+
+
+def test_noalloc_descriptor_under_graph_capture():
+    """The callers this builder is for capture their launches: a forward with
+    a no-alloc descriptor is captured in a HIP graph and replayed four times,
+    with new inputs, unrelated eager work and synchronisations in between;
+    every replay equals the eager launch with the allocating builder's
+    descriptor bitwise."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    w = workloads.custom([150, 150, 40, 40], [700, 700, 300, 300], 4, 128, seed=7310, name="noalloc_graph")
+    na = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, "bf16", noalloc=True)
+    ref = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, "bf16")
+    cu = torch.from_numpy(na.cu_seqlens).cuda()
+    q, k, v = (x.cuda() for x in workloads.bf16_inputs(w))
+    out = torch.empty_like(q)
+    scale = 1 / math.sqrt(w.head_dim)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm-up outside the capture
+        pva.packed_attn_fwd(q, k, v, cu, na, scale, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pva.packed_attn_fwd(q, k, v, cu, na, scale, out)
+    gen = torch.Generator(device="cuda").manual_seed(7311)
+    for i in range(4):
+        if i > 0:
+            for x in (q, k, v):
+                x.copy_(torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        want = torch.empty_like(q)
+        pva.packed_attn_fwd(q, k, v, cu, ref, scale, want)
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), f"replay {i} differs from the eager launch"
+        torch.randn(1 << 20, device="cuda").sum().item()
+    say("[noalloc] graph: 4 replays equal to eager")
