@@ -84,6 +84,10 @@ def parse():
                     help="summarise a rocprofv3 counter file of a --kernel-only run (MFMA busy and co-issue "
                          "cycles, LDS bank conflicts, L2 hits, instruction counts) and one of the derived "
                          "MfmaUtil counter (no GPU needed); prints the counter record for --workload")
+    ap.add_argument("--stall-summary", nargs=2, metavar=("WAVE_CSV", "ISSUE_CSV"),
+                    help="summarise two rocprofv3 counter files of --kernel-only runs: wave states (resident, "
+                         "waiting, issuing) and the MFMA pipe's busy cycles with the shader clock (no GPU needed); "
+                         "prints the stall record for --workload")
     return ap.parse_args()
 
 
@@ -225,6 +229,74 @@ def counter_summary(args):
     print("\n".join(lines))
 
 
+STALL_WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY",
+                       "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "GRBM_GUI_ACTIVE")
+STALL_ISSUE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
+                        "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
+MFMA_FLOPS = {"bf16": 2 * 32 * 32 * 16, "fp8": 2 * 32 * 32 * 64}  # per 32x32 MFMA instruction
+PEAK_CLOCK_GHZ = 2.4
+
+
+def stall_summary(args):
+    """Where the waves of the attention kernel spend their resident cycles
+    (SQ wave-state counters, sampled every 4 cycles per wave), and the
+    decomposition of the fraction of the MFMA peak into the MFMA pipe's busy
+    share, the shader clock against the 2.4 GHz the peak assumes, and the
+    useful share of the executed MFMA FLOPs."""
+    import csv
+    wave_csv, issue_csv = args.stall_summary
+    w = workloads.WORKLOADS[args.workload]()
+    if isinstance(w, workloads.SegWorkload):
+        sys.exit("stall summary: mixed text/image workloads only")
+    dtype = "fp8" if w.dtype == "fp8" else "bf16"
+    tag = f"fwd_{dtype}_kernel"
+
+    def load(path, names):
+        vals, durations = {}, {}
+        with open(path, newline="") as f:
+            for row in csv.DictReader(f):
+                if tag not in row["Kernel_Name"]:
+                    continue
+                vals.setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+                durations[row["Dispatch_Id"]] = int(row["End_Timestamp"]) - int(row["Start_Timestamp"])
+        missing = [c for c in names if c not in vals]
+        if missing:
+            sys.exit(f"stall summary: no {tag} dispatch with {missing} in {path}")
+        return {c: statistics.fmean(v) for c, v in vals.items()}, durations
+
+    a, _ = load(wave_csv, STALL_WAVE_COUNTERS)
+    b, dur_b = load(issue_csv, STALL_ISSUE_COUNTERS)
+    cyc_a = a["GRBM_GUI_ACTIVE"] / NUM_XCD
+    cyc_b = b["GRBM_GUI_ACTIVE"] / NUM_XCD
+    wave_cycles = 4.0 * a["SQ_WAVE_CYCLES"]
+    share = lambda c: 100.0 * 4.0 * a[c] / wave_cycles  # noqa: E731
+    clock = cyc_b / min(dur_b.values())
+    busy = b["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_SIMD * cyc_b)
+    useful = 4.0 * w.head_dim * w.num_heads * sum(
+        t * (t + 1) // 2 + i * (t + i) for t, i in zip(w.text_len, w.image_len))
+    useful_share = useful / (b["SQ_INSTS_MFMA"] * MFMA_FLOPS[dtype])
+    lines = [
+        f"kernel: {tag}",
+        f"workload: {w.name}",
+        f"source_sha256_16: {kernel_source_hash(dtype)}",
+        f"resident_waves_per_simd: {wave_cycles / (NUM_SIMD * cyc_a):.2f}",
+        f"issuing_pct_of_wave_cycles: {share('SQ_ACTIVE_INST_ANY'):.1f}",
+        f"waiting_to_issue_pct_of_wave_cycles: {share('SQ_WAIT_INST_ANY'):.1f}",
+        f"waiting_on_counters_or_barrier_pct_of_wave_cycles: {share('SQ_WAIT_ANY'):.1f}",
+        f"lds_data_fifo_full_cycles: {a['SQ_LDS_DATA_FIFO_FULL']:.0f}",
+        f"lds_cmd_fifo_full_pct_of_cu_cycles: {100.0 * a['SQ_LDS_CMD_FIFO_FULL'] / (256 * cyc_a):.2f}",
+        f"valu_active_pct_of_wave_cycles: {100.0 * 4.0 * b['SQ_ACTIVE_INST_VALU'] / wave_cycles:.1f}",
+        f"waiting_for_lds_issue_pct_of_wave_cycles: {100.0 * 4.0 * b['SQ_WAIT_INST_LDS'] / wave_cycles:.1f}",
+        f"valu_instructions_per_mfma: {b['SQ_INSTS_VALU'] / b['SQ_INSTS_MFMA']:.2f}",
+        f"mfma_busy_pct: {100.0 * busy:.1f}",
+        f"shader_clock_ghz_fastest_dispatch: {clock:.3f}",
+        f"clock_share_of_{PEAK_CLOCK_GHZ}_ghz: {clock / PEAK_CLOCK_GHZ:.3f}",
+        f"useful_share_of_mfma_flops: {useful_share:.3f}",
+        f"frac_from_counters: {busy * clock / PEAK_CLOCK_GHZ * useful_share:.3f}",
+    ]
+    print("\n".join(lines))
+
+
 def stored_counters(dtype, workload):
     """Counter record for this kernel and workload if taken on the current
     sources, else None."""
@@ -304,6 +376,9 @@ def main():
         return
     if args.counter_summary:
         counter_summary(args)
+        return
+    if args.stall_summary:
+        stall_summary(args)
         return
 
     import torch

@@ -22,11 +22,11 @@
 //   accumulators into the B operand of PV; probabilities stay <= 2^8.75,
 //   inside the format's range.
 //   O^T[d, q] += V^T P^T    A = V^T read with ds_read_b64_tr_b8 (8 keys of
-//                           one column per read); a fifth 32-row block whose A
-//                           operand is all ones accumulates l = sum of the
-//                           quantised probabilities, i.e. exactly the weights
-//                           PV applied, so every output row is a convex
-//                           combination of V rows.
+//                           one column per read); one 16x16x128 MFMA on the
+//                           same P operand (rowsum_fp8 below) accumulates
+//                           l = sum of the quantised probabilities, i.e.
+//                           exactly the weights PV applied, so every output
+//                           row is a convex combination of V rows.
 //   a tile in which some row's largest probability may carry a sizeable
 //   share of that row's weight (kResidualFactor below) gets a second PV pass
 //   with the probabilities' E4M3 residuals.
@@ -113,6 +113,18 @@ struct VSwizzledPairs {
 __device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
   // E4M3 x E4M3 (format code 0 for both operands), no block scales
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Row sums of a probability operand on one 16x16x128 E4M3 MFMA (half the
+// cycles of a 32x32x64 block). As a 16x16x128 B operand, lane l's 32 bytes
+// form column l % 16 for the l / 16-th quarter of the contraction; they are
+// the probabilities of query l % 32, so columns c and c + 16 each collect two
+// queries' halves. The selector A holds E4M3 1.0 where row r and quarter
+// l / 16 agree in parity (bit 2 of r against bit 0 of the quarter), else 0:
+// output rows 4 (l / 16) .. +3 of column l % 16, which lane l receives, then
+// hold the full sum of query l % 32 in all four of its registers.
+__device__ __forceinline__ f32x4 rowsum_fp8(const i32x8& sel, const i32x8& p, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(sel, p, c, 0, 0, 0, 0, 0, 0);
 }
 
 struct Fp8Kernel {
@@ -219,17 +231,17 @@ struct Fp8Kernel {
     pin(pb);
   }
 
-  // PV(j) MFMAs (the ones block first, so that the row sum is complete early,
-  // then the NDB column blocks), one V^T operand read ahead, each followed by
+  // PV(j) MFMAs (the row sum first, so that it is complete early, then the
+  // NDB column blocks), one V^T operand read ahead, each followed by
   // a slice of the row max of tile j+1 (raw scores)
-  static __device__ __forceinline__ float pv_with_max(f32x16 (&o)[NDB + 1], const uint8_t* vst, const i32x8& pb,
-                                                      const i32x8& ones, const f32x16 (&snext)[NB],
+  static __device__ __forceinline__ float pv_with_max(f32x16 (&o)[NDB], f32x4& l, const uint8_t* vst,
+                                                      const i32x8& pb, const i32x8& sel, const f32x16 (&snext)[NB],
                                                       const int (&vrow0)[1], int vsw, int half, int p8) {
     constexpr int NMAX = (NB * 16 - 2) / 2;  // max3 operations over the tile's 32 scores (after the first)
     constexpr int PER = (NMAX + NDB - 1) / NDB;
     float mx = max3(snext[0][0], snext[0][1], snext[0][2]);
     i32x8 va = read_v(vst, 0, vrow0, vsw, half, p8);
-    o[NDB] = mfma_fp8(ones, pb, o[NDB]);
+    l = rowsum_fp8(sel, pb, l);
     // keeps the scheduler from sinking the row-sum MFMA to the end of the
     // phase, where the residual test would wait for its result
     __builtin_amdgcn_sched_barrier(0);
@@ -254,8 +266,8 @@ struct Fp8Kernel {
 
   // second PV pass with the E4M3 residuals of a tile's probabilities (the
   // fp32 probabilities pf, minus their E4M3 values pb)
-  static __device__ __forceinline__ void pv_residual(f32x16 (&o)[NDB + 1], const uint8_t* vst,
-                                                     const float (&pf)[NB * 16], const i32x8& pb, const i32x8& ones,
+  static __device__ __forceinline__ void pv_residual(f32x16 (&o)[NDB], f32x4& l, const uint8_t* vst,
+                                                     const float (&pf)[NB * 16], const i32x8& pb, const i32x8& sel,
                                                      const int (&vrow0)[1], int vsw, int half, int p8) {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     i32x8 pl;
@@ -268,7 +280,7 @@ struct Fp8Kernel {
     }
 #pragma unroll
     for (int db = 0; db < NDB; ++db) o[db] = mfma_fp8(read_v(vst, db, vrow0, vsw, half, p8), pl, o[db]);
-    o[NDB] = mfma_fp8(ones, pl, o[NDB]);
+    l = rowsum_fp8(sel, pl, l);
   }
 
   static __device__ __forceinline__ void pin(i32x8& pb) {
@@ -381,18 +393,22 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
       qf[c] = i32x8{};
   }
 
-  // O^T accumulators; block NDB accumulates l (ones operand)
-  f32x16 oacc[NDB + 1];
+  // O^T accumulators and the row sums l of the weights PV applied
+  f32x16 oacc[NDB];
 #pragma unroll
-  for (int db = 0; db <= NDB; ++db) oacc[db] = f32x16{};
-  i32x8 ones;
+  for (int db = 0; db < NDB; ++db) oacc[db] = f32x16{};
+  f32x4 lacc = {};
+  i32x8 sel;
+  {
+    const int sel4 = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? 0x38383838 : 0;  // E4M3 1.0 per byte, or 0
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    // E4M3 1.0 in every byte, written by an opaque move: as a known constant
-    // the compiler would re-create the 8-register operand every tile
-    int one4;
-    asm volatile("v_mov_b32 %0, 0x38383838" : "=v"(one4));
-    ones[w] = one4;
+    for (int w = 0; w < 8; ++w) {
+      // opaque copies: as a known value the compiler would rebuild the
+      // 8-register operand every tile
+      int t = sel4;
+      asm volatile("" : "+v"(t));
+      sel[w] = t;
+    }
   }
   // The row's reference max m (log2 units) is kept as the derived values the
   // tile loop uses: the exponent bias mb = m - kP8Shift of the probabilities
@@ -450,22 +466,24 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, mb, pb, pf, kad);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
-    const float mt = Kn::pv_with_max(oacc, vst[SJ], pb, ones, snext, vrow0, vsw, half, p8);
+    const float mt = Kn::pv_with_max(oacc, lacc, vst[SJ], pb, sel, snext, vrow0, vsw, half, p8);
     // residual pass when a key of this tile may carry 1/kResidualFactor of
     // its row's weight: kResidualFactor times the tile's largest probability
     // against the row's sum so far, this tile included (a row without keys
     // has 0 against 0 and never asks for it)
-    if (__builtin_expect(wave_any(fast_exp2(fmaf(tmax, scale_log2, -mres)) > oacc[NDB][0]), 0))
-      Kn::pv_residual(oacc, vst[SJ], pf, pb, ones, vrow0, vsw, half, p8);
+    if (__builtin_expect(wave_any(fast_exp2(fmaf(tmax, scale_log2, -mres)) > lacc[0]), 0))
+      Kn::pv_residual(oacc, lacc, vst[SJ], pf, pb, sel, vrow0, vsw, half, p8);
     tmax = mt;
     const bool need = mt > thr;
     if (__builtin_expect(wave_any(need), 0)) {
       const float mtl = mt * scale_log2;
       const float alpha = need ? fast_exp2(m_run - mtl) : 1.0f;
 #pragma unroll
-      for (int db = 0; db <= NDB; ++db)
+      for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lacc[i] *= alpha;
       if (need) set_reference(mtl);
     }
     wait_vmcnt<2 * Cfg::DMA_MIN>();
@@ -501,12 +519,12 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   // workgroup ends and its LDS is handed to another
   wait_vmcnt<0>();
 
-  // ---- epilogue: O = O^T * v_s / l (l from the ones block), bf16, or fp32
+  // ---- epilogue: O = O^T * v_s / l (l from the row-sum MFMA), bf16, or fp32
   // for partial results; optionally the row's log-sum-exp of the scaled
   // scores, ln 2 * (m + log2 l - kP8Shift) with l the sum of the weights PV applied
   // (-inf for a row with no key in range)
   if (wave_active && qrow < qend) {
-    const float lt = oacc[NDB][0];
+    const float lt = lacc[0];
     const float inv = lt > 0.0f ? vs / lt : 0.0f;
     const int64_t orow = qbase + int64_t(qrow) * rs;
     if (out_f32) {
