@@ -233,7 +233,8 @@ STALL_WAVE_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_
                        "SQ_LDS_DATA_FIFO_FULL", "SQ_LDS_CMD_FIFO_FULL", "GRBM_GUI_ACTIVE")
 STALL_ISSUE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU",
                         "SQ_ACTIVE_INST_LDS", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
-MFMA_FLOPS = {"bf16": 2 * 32 * 32 * 16, "fp8": 2 * 32 * 32 * 64}  # per 32x32 MFMA instruction
+# dense MFMA FLOPs per busy cycle of one SIMD's matrix pipe (the peak over 1024 SIMDs at 2.4 GHz)
+MFMA_FLOPS_PER_CYCLE = {"bf16": 1024, "fp8": 2048}
 PEAK_CLOCK_GHZ = 2.4
 
 
@@ -274,7 +275,7 @@ def stall_summary(args):
     busy = b["SQ_VALU_MFMA_BUSY_CYCLES"] / (NUM_SIMD * cyc_b)
     useful = 4.0 * w.head_dim * w.num_heads * sum(
         t * (t + 1) // 2 + i * (t + i) for t, i in zip(w.text_len, w.image_len))
-    useful_share = useful / (b["SQ_INSTS_MFMA"] * MFMA_FLOPS[dtype])
+    useful_share = useful / (b["SQ_VALU_MFMA_BUSY_CYCLES"] * MFMA_FLOPS_PER_CYCLE[dtype])
     lines = [
         f"kernel: {tag}",
         f"workload: {w.name}",
@@ -288,19 +289,19 @@ def stall_summary(args):
         f"valu_active_pct_of_wave_cycles: {100.0 * 4.0 * b['SQ_ACTIVE_INST_VALU'] / wave_cycles:.1f}",
         f"waiting_for_lds_issue_pct_of_wave_cycles: {100.0 * 4.0 * b['SQ_WAIT_INST_LDS'] / wave_cycles:.1f}",
         f"valu_instructions_per_mfma: {b['SQ_INSTS_VALU'] / b['SQ_INSTS_MFMA']:.2f}",
+        f"mfma_busy_cycles_per_instruction: {b['SQ_VALU_MFMA_BUSY_CYCLES'] / b['SQ_INSTS_MFMA']:.1f}",
         f"mfma_busy_pct: {100.0 * busy:.1f}",
         f"shader_clock_ghz_fastest_dispatch: {clock:.3f}",
         f"clock_share_of_{PEAK_CLOCK_GHZ}_ghz: {clock / PEAK_CLOCK_GHZ:.3f}",
-        f"useful_share_of_mfma_flops: {useful_share:.3f}",
+        f"useful_share_of_mfma_busy_flops: {useful_share:.3f}",
         f"frac_from_counters: {busy * clock / PEAK_CLOCK_GHZ * useful_share:.3f}",
     ]
     print("\n".join(lines))
 
 
-def stored_counters(dtype, workload):
-    """Counter record for this kernel and workload if taken on the current
-    sources, else None."""
-    path = counters_file(dtype, workload)
+def _stored_record(path, dtype, keys):
+    """The named float fields of a stored counter record if it was taken on
+    the current kernel sources, else None."""
     if not os.path.exists(path):
         return None
     rec = {}
@@ -311,12 +312,32 @@ def stored_counters(dtype, workload):
                 rec[key.strip()] = val.strip()
     if rec.get("source_sha256_16") != kernel_source_hash(dtype):
         return None
-    keys = ("mfma_busy_pct", "valu_coissue_pct_of_mfma_busy", "valu_instructions_per_mfma",
-            "lds_bank_conflict_cycles", "l2_hit_pct", "shader_clock_ghz_fastest_dispatch")
     try:
         return {k: float(rec[k]) for k in keys}
     except (KeyError, ValueError):
         return None
+
+
+def stalls_file(dtype, workload):
+    return os.path.join(PROFILES, f"stalls_fwd_{dtype}_{workload}.txt")
+
+
+def stored_counters(dtype, workload):
+    """Counter record for this kernel and workload if taken on the current
+    sources, else None; with the wave-state record under "stalls" when one
+    matches too."""
+    ctr = _stored_record(counters_file(dtype, workload), dtype,
+                         ("mfma_busy_pct", "valu_coissue_pct_of_mfma_busy", "valu_instructions_per_mfma",
+                          "lds_bank_conflict_cycles", "l2_hit_pct", "shader_clock_ghz_fastest_dispatch"))
+    stalls = _stored_record(stalls_file(dtype, workload), dtype,
+                            ("resident_waves_per_simd", "issuing_pct_of_wave_cycles",
+                             "waiting_to_issue_pct_of_wave_cycles",
+                             "waiting_on_counters_or_barrier_pct_of_wave_cycles",
+                             f"clock_share_of_{PEAK_CLOCK_GHZ}_ghz", "useful_share_of_mfma_busy_flops",
+                             "frac_from_counters"))
+    if ctr and stalls:
+        ctr["stalls"] = stalls
+    return ctr
 
 
 def algorithmic_bytes(w):

@@ -96,6 +96,51 @@ def test_counter_summary_ratios(tmp_path, capsys):
     assert float(rec["mfma_util_derived_pct"]) == pytest.approx(49.0)
 
 
+def _timed_csv(path, kernel, vals, ns):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(HEADER)
+        for i, (counter, value) in enumerate(vals.items()):
+            w.writerow([i, 7, "Agent 1", 1, 1, 1, 256, 1, kernel, 256, 0, 0, 8, 0, 16, counter, value, 0, ns])
+
+
+def test_stall_summary_decomposes_the_fraction_of_peak(tmp_path, capsys):
+    import workloads
+    k = "_ZN3pva12_GLOBAL__N_115fwd_bf16_kernelILi128EEEv"
+    w = workloads.WORKLOADS["mixed_res"]()
+    useful = 4 * w.head_dim * w.num_heads * sum(t * (t + 1) // 2 + i * (t + i)
+                                                  for t, i in zip(w.text_len, w.image_len))
+    cycles = 2.4e6  # shader cycles per XCD; 2 ms at 1.2 GHz
+    busy = useful / 1024  # busy cycles whose every FLOP is useful
+    wave = {"GRBM_GUI_ACTIVE": 8 * cycles, "SQ_WAVE_CYCLES": 2.5 * 1024 * cycles / 4,
+            "SQ_WAIT_ANY": 0.25 * 2.5 * 1024 * cycles / 4, "SQ_WAIT_INST_ANY": 0.5 * 2.5 * 1024 * cycles / 4,
+            "SQ_ACTIVE_INST_ANY": 0.25 * 2.5 * 1024 * cycles / 4, "SQ_LDS_DATA_FIFO_FULL": 0.0,
+            "SQ_LDS_CMD_FIFO_FULL": 0.0}
+    issue = {"GRBM_GUI_ACTIVE": 8 * cycles, "SQ_VALU_MFMA_BUSY_CYCLES": busy, "SQ_INSTS_MFMA": busy / 32,
+             "SQ_INSTS_VALU": 5 * busy / 32, "SQ_ACTIVE_INST_VALU": 1.0, "SQ_ACTIVE_INST_LDS": 1.0,
+             "SQ_WAIT_INST_LDS": 0.0}
+    _timed_csv(tmp_path / "a.csv", k, wave, 2_000_000)
+    _timed_csv(tmp_path / "b.csv", k, issue, 2_000_000)
+
+    class A:
+        workload = "mixed_res"
+        stall_summary = [str(tmp_path / "a.csv"), str(tmp_path / "b.csv")]
+    bench.stall_summary(A)
+    rec = dict(line.split(": ", 1) for line in capsys.readouterr().out.strip().splitlines())
+    assert float(rec["resident_waves_per_simd"]) == pytest.approx(2.5)
+    assert float(rec["waiting_to_issue_pct_of_wave_cycles"]) == pytest.approx(50.0)
+    assert float(rec["waiting_on_counters_or_barrier_pct_of_wave_cycles"]) == pytest.approx(25.0)
+    assert float(rec["shader_clock_ghz_fastest_dispatch"]) == pytest.approx(1.2)
+    assert float(rec["clock_share_of_2.4_ghz"]) == pytest.approx(0.5)
+    assert float(rec["useful_share_of_mfma_busy_flops"]) == pytest.approx(1.0)
+    assert float(rec["mfma_busy_cycles_per_instruction"]) == pytest.approx(32.0)
+    busy_share = float(rec["mfma_busy_pct"]) / 100
+    assert float(rec["frac_from_counters"]) == pytest.approx(busy_share * 0.5, abs=1e-3)
+    # the same product is the useful FLOPs over the peak's FLOPs in the counted duration
+    peak_flops = bench.PEAK_TFLOPS["bf16"] * 1e12 * 2e-3
+    assert float(rec["frac_from_counters"]) == pytest.approx(useful / peak_flops, rel=2e-3)
+
+
 def test_stored_counters_require_current_sources(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     path = bench.counters_file("fp8", "wl")
