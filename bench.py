@@ -75,6 +75,10 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=1,
                     help="P > 1: split every sequence's keys into P equal chunks; one step is P partial launches "
                          "(fp32 O + log-sum-exp) and one merge (two-segment bf16 workloads)")
+    ap.add_argument("--fused", action="store_true",
+                    help="with --split-keys P >= 2: fold each chunk into a running result "
+                         "(packed_attn_fwd_partial for the first chunk, packed_attn_fwd_partial_accumulate for the "
+                         "others, the last one writing bf16 O) instead of P fp32 partials and a merge")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
@@ -694,7 +698,8 @@ def config_record(key, steps, warmup):
 def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     """Ring attention's single-GPU half on the workload: each sequence's keys
     split into P equal chunks (their K/V copied apart beforehand, as a rank
-    would hold them), one partial launch per chunk, then one merge. fp8
+    would hold them), one partial launch per chunk, then one merge; or, with
+    --fused, each chunk folded into a running result by its own launch. fp8
     workloads pass their (q, k, v) scales; K/V chunks keep their sequence's."""
     import torch
     import packed_varlen_masked_attn_amd as pva
@@ -721,8 +726,31 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     stream = torch.cuda.current_stream()
 
     part_out = [(o_parts[p], l_parts[p]) for p in range(P)]
+    fused = args.fused
+    if fused and P < 2:
+        sys.exit("--fused needs --split-keys 2 or more")
+
+    def fused_step(ev=None):
+        o_acc, l_acc = part_out[0]
+        for p, (d, kp, vp, cuk) in enumerate(parts):
+            dst = out if p == P - 1 else None
+            if fp8_scales is not None:
+                if p == 0:
+                    pva.packed_attn_fwd_partial_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, o_acc, l_acc, stream)
+                else:
+                    pva.packed_attn_fwd_partial_accumulate_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, o_acc,
+                                                               l_acc, dst, stream)
+            elif p == 0:
+                pva.packed_attn_fwd_partial(q, kp, vp, cuq, cuk, d, scale, o_acc, l_acc, stream)
+            else:
+                pva.packed_attn_fwd_partial_accumulate(q, kp, vp, cuq, cuk, d, scale, o_acc, l_acc, dst, stream)
+        if ev is not None:
+            ev.record(stream)
 
     def step(ev=None):
+        if fused:
+            fused_step(ev)
+            return
         for (d, kp, vp, cuk), (op, lp) in zip(parts, part_out):
             if fp8_scales is not None:
                 pva.packed_attn_fwd_partial_fp8(q, kp, vp, *fp8_scales, cuq, cuk, d, scale, op, lp, stream)
@@ -753,11 +781,31 @@ def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):
     merge_ms = statistics.fmean(merges_all)
     ms_per_step = wall * 1e3 / args.steps
     value = flops * args.steps / wall / 1e12
+    achieved = flops / (part_ms * 1e-3) / 1e12
+    if fused:
+        log(f"[bench] split keys x{P}, fused: {ms_per_step:.4f} ms/step (launches {part_ms:.4f} ms, median "
+            f"{statistics.median(parts_all):.4f}, max {max(parts_all):.4f}) -> {value:.1f} useful TFLOP/s")
+        print(json.dumps({
+            "metric": "useful attention TFLOP/s, key-split chunks folded into a running result "
+                      "(Ring attention's single-GPU half)",
+            "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": dtype, "data": "synthetic (seeded N(0,1) Q/K/V of the workload's shapes)",
+            "config": {"workload": w.name, "split_keys": P, "fused": True, "text_len": list(w.text_len),
+                       "image_len": list(w.image_len), "num_heads": H, "head_dim": D, "parallelism": "single GPU"},
+            "launches_ms": round(part_ms, 5),
+            "launches_ms_median_p90": [round(statistics.median(parts_all), 5), round(pct(parts_all, 90), 5)],
+            "desc_build_us": round(desc_us, 1),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[dtype],
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS[dtype], 4), "traffic": None,
+                         "kernel": ("fwd_fp8_kernel" if dtype == "fp8" else f"fwd_bf16_kernel<{D}>") +
+                                   " (all chunk launches)"},
+        }), flush=True)
+        return
     merge_bytes = N * H * (P * (4 * D + 4) + 2 * D)
     log(f"[bench] split keys x{P}: {ms_per_step:.4f} ms/step (partials {part_ms:.4f} ms, median "
         f"{statistics.median(parts_all):.4f}, max {max(parts_all):.4f}; merge {merge_ms:.4f} ms) "
         f"-> {value:.1f} useful TFLOP/s; merge {merge_bytes / merge_ms / 1e6:.0f} GB/s")
-    achieved = flops / (part_ms * 1e-3) / 1e12
     print(json.dumps({
         "metric": "useful attention TFLOP/s, key-split partials + merge (Ring attention's single-GPU half)",
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

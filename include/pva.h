@@ -309,6 +309,40 @@ int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, con
                                 float* out_f32, float* lse, void* stream);
 
 /*
+ * Partial forward over one key chunk that folds the chunk into a running
+ * result, the online form of the combining step of Ring attention
+ * ("[RFC]: HunyuanImage 3.0 deployment", Proposed Change P2): per queried
+ * row, with (O_c, lse_c) this chunk's partial result as packed_attn_fwd_partial
+ * would write it and (O_acc, lse_acc) the running one,
+ *   lse = log(exp(lse_acc) + exp(lse_c)),
+ *   O   = exp(lse_acc - lse) O_acc + exp(lse_c - lse) O_c.
+ *   o_acc   : device float [total_q, H, D], 16-byte aligned: the running O
+ *             (from packed_attn_fwd_partial or an earlier call of this one)
+ *   lse_acc : device float [total_q, H], 4-byte aligned: its log-sum-exp;
+ *             -inf marks a row no chunk has given a key yet, whose o_acc row
+ *             is then not read (it may hold anything)
+ *   out     : NULL: the merged O goes back to o_acc; else device bf16
+ *             [total_q, H, D], 16-byte aligned, disjoint from o_acc and
+ *             lse_acc: the merged O goes there in bf16 (the last chunk) and
+ *             o_acc is left as it was
+ * lse_acc receives the merged log-sum-exp in both cases. Starting from
+ * lse_acc = -inf everywhere, one call per chunk gives the result of
+ * packed_attn_fwd_partial + pva_merge_partials without the per-chunk fp32
+ * outputs and the merge pass. Calls on one o_acc must be ordered (one
+ * stream). Other arguments and errors as packed_attn_fwd_partial.
+ */
+int packed_attn_fwd_partial_accumulate(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                       float* o_acc, float* lse_acc, void* out, void* stream);
+
+/* FP8 variant of packed_attn_fwd_partial_accumulate (inputs and scales as in
+ * packed_attn_fwd_partial_fp8). */
+int packed_attn_fwd_partial_accumulate_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                           const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                           float* o_acc, float* lse_acc, void* out, void* stream);
+
+/*
  * Forward with K and V in a paged pool (the scheduler-managed paged KV mode
  * of "HunyuanImage-3.0-Instruct DiT Image Generation on 4x GPU", section
  * "Scheduler-managed paged KV": unquantised bf16 K/V in a fixed physical

@@ -33,7 +33,8 @@ EXPORTED = [
     "pva_seg_desc_free", "packed_attn_fwd", "packed_attn_fwd_fp8", "packed_attn_fwd_varlen",
     "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
     "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials", "packed_attn_fwd_paged",
-    "packed_attn_fwd_partial_fp8", "pva_seg_desc_build_noalloc",
+    "packed_attn_fwd_partial_fp8", "pva_seg_desc_build_noalloc", "packed_attn_fwd_partial_accumulate",
+    "packed_attn_fwd_partial_accumulate_fp8",
 ]
 
 
@@ -79,6 +80,9 @@ def lib() -> ctypes.CDLL:
                                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int, ctypes.POINTER(vp)], ctypes.c_int)
     sig("packed_attn_fwd_partial", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp], ctypes.c_int)
     sig("packed_attn_fwd_partial_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_partial_accumulate", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp], ctypes.c_int)
+    sig("packed_attn_fwd_partial_accumulate_fp8",
+        [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp, vp, vp], ctypes.c_int)
     sig("packed_attn_fwd_paged", [vp, vp, vp, vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp, vp,
                                         ctypes.c_float, vp, vp], ctypes.c_int)
     sig("pva_merge_partials", [vp, vp, ctypes.c_int32, ctypes.c_int64, ctypes.c_int32, vp, vp, vp], ctypes.c_int)
@@ -441,6 +445,63 @@ def packed_attn_fwd_partial_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q
                                            ctypes.c_void_p(_stream_handle(stream)))
     _check(st)
     return out_f32, lse
+
+
+def _check_accumulate_out(desc: SegDesc, o_acc, lse_acc, out) -> None:
+    import torch
+    _check_partial_out(desc, o_acc, lse_acc)
+    Nq, H, D = desc.total_q, desc.num_heads, desc.head_dim
+    if out is not None and (not isinstance(out, torch.Tensor) or not out.is_cuda or out.dtype != torch.bfloat16
+                            or tuple(out.shape) != (Nq, H, D) or not out.is_contiguous()):
+        raise PvaError(PVA_ERR_INVALID_ARG, f"out must be None or a contiguous device bf16 [{Nq}, {H}, {D}] tensor")
+
+
+def packed_attn_fwd_partial_accumulate(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc: SegDesc, scale: float, o_acc,
+                                       lse_acc, out=None, stream=None):
+    """bf16 key-chunk forward folded into a running result: o_acc (float32
+    [total_q, H, D]) and lse_acc (float32 [total_q, H], -inf where no chunk has
+    given a key yet) are updated in place, or with `out` (bf16 [total_q, H, D])
+    the merged O is written there instead (the last chunk). Returns out if
+    given, else o_acc."""
+    import torch
+    Nq, H, D = seg_desc.total_q, seg_desc.num_heads, seg_desc.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        N = Nq if name == "q" else seg_desc.total_tokens
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype != torch.bfloat16 or tuple(t.shape) != (N, H, D)
+                or not t.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a contiguous device bf16 [{N}, {H}, {D}] tensor")
+    _check_accumulate_out(seg_desc, o_acc, lse_acc, out)
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_partial_accumulate(_ptr(q), _ptr(k), _ptr(v), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                                  seg_desc.handle, ctypes.c_float(scale), _ptr(o_acc), _ptr(lse_acc),
+                                                  _ptr(out) if out is not None else None,
+                                                  ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out if out is not None else o_acc
+
+
+def packed_attn_fwd_partial_accumulate_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k,
+                                           seg_desc: SegDesc, scale: float, o_acc, lse_acc, out=None, stream=None):
+    """fp8 variant of packed_attn_fwd_partial_accumulate."""
+    import torch
+    Nq, H, D = seg_desc.total_q, seg_desc.num_heads, seg_desc.head_dim
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        N = Nq if name == "q" else seg_desc.total_tokens
+        if (not isinstance(t, torch.Tensor) or not t.is_cuda or t.dtype not in (torch.float8_e4m3fn, torch.uint8)
+                or tuple(t.shape) != (N, H, D) or not t.is_contiguous()):
+            raise PvaError(PVA_ERR_INVALID_ARG, f"{name} must be a contiguous device E4M3 [{N}, {H}, {D}] tensor")
+    _check_accumulate_out(seg_desc, o_acc, lse_acc, out)
+    _check_scales(seg_desc, (("q_scale", q_scale), ("k_scale", k_scale), ("v_scale", v_scale)))
+    _check_cu(seg_desc, cu_seqlens_q, "cu_seqlens_q")
+    _check_cu(seg_desc, cu_seqlens_k, "cu_seqlens_k")
+    st = lib().packed_attn_fwd_partial_accumulate_fp8(_ptr(q), _ptr(k), _ptr(v), _ptr(q_scale), _ptr(k_scale),
+                                                      _ptr(v_scale), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                                                      seg_desc.handle, ctypes.c_float(scale), _ptr(o_acc),
+                                                      _ptr(lse_acc), _ptr(out) if out is not None else None,
+                                                      ctypes.c_void_p(_stream_handle(stream)))
+    _check(st)
+    return out if out is not None else o_acc
 
 
 def packed_attn_fwd_paged(q, k_pool, v_pool, block_table, cu_seqlens_q, seg_desc: SegDesc, scale: float, out,

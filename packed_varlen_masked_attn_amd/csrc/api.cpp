@@ -15,12 +15,12 @@
 
 namespace pva {
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream);
+                    float scale, const OutSpec& out, const PagedKV* paged, hipStream_t stream);
 int launch_merge(const float* o_parts, const float* lse_parts, int n_parts, int64_t rows, int head_dim, void* out,
                  float* lse_out, hipStream_t stream);
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks,
-                   const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, void* out, int out_f32,
-                   float* lse, hipStream_t stream);
+                   const float* vs, const int32_t* cu, const pva_seg_desc* d, float scale, const OutSpec& out,
+                   hipStream_t stream);
 }  // namespace pva
 
 namespace {
@@ -176,28 +176,56 @@ int build_segs(const int32_t* seg_len, const int32_t* seg_kind, const int32_t* s
 }
 
 int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, const int32_t* cu_k,
-             const pva_seg_desc* d, float scale, void* out, int out_f32, float* lse, void* stream) {
-  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_BF16);
+             const pva_seg_desc* d, float scale, const pva::OutSpec& out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out.o, PVA_BF16);
   if (st != PVA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, out_f32, lse, nullptr, s);
+  st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, nullptr, s);
   if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
   return ok();
 }
 
 int fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, const float* k_scale,
             const float* v_scale, const int32_t* cu_q, const int32_t* cu_k, const pva_seg_desc* d, float scale,
-            void* out, int out_f32, float* lse, void* stream) {
-  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out, PVA_FP8_E4M3);
+            const pva::OutSpec& out, void* stream) {
+  int st = validate_fwd(q, k, v, cu_q, cu_k, d, scale, out.o, PVA_FP8_E4M3);
   if (st != PVA_OK) return st;
   if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
-  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, out_f32, lse, s);
+  st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, s);
   if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
   if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
   return ok();
+}
+
+// Output of a launch that writes a plain bf16 result.
+pva::OutSpec plain_out(void* out) { return pva::OutSpec{out, 0, nullptr, nullptr, nullptr}; }
+
+// Output of an accumulating key-chunk launch: the running result is read from
+// (o_acc, lse_acc) and the merged one written back to them, or, with `out`,
+// O goes to out in bf16 (lse_acc is updated either way).
+int accumulate_out(const pva_seg_desc* d, float* o_acc, float* lse_acc, void* out, pva::OutSpec* spec) {
+  if (!d) return set_error(PVA_ERR_INVALID_ARG, "seg_desc is NULL");
+  if (!o_acc || !lse_acc) return set_error(PVA_ERR_INVALID_ARG, "o_acc or lse_acc is NULL");
+  if (!aligned16(o_acc)) return set_error(PVA_ERR_INVALID_ARG, "o_acc must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(lse_acc) & 3u) != 0)
+    return set_error(PVA_ERR_INVALID_ARG, "lse_acc must be 4-byte aligned");
+  if (out) {
+    // other rows' running values must not be overwritten before they are read
+    const uintptr_t elems = uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads) * uintptr_t(d->plan.head_dim);
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(out), a1 = a0 + 2 * elems;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(o_acc), b1 = b0 + 4 * elems;
+    const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse_acc),
+                    l1 = l0 + 4 * uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads);
+    if ((a0 < b1 && b0 < a1) || (a0 < l1 && l0 < a1))
+      return set_error(PVA_ERR_INVALID_ARG, "out overlaps o_acc or lse_acc");
+    *spec = pva::OutSpec{out, 0, lse_acc, o_acc, lse_acc};
+  } else {
+    *spec = pva::OutSpec{o_acc, 1, lse_acc, o_acc, lse_acc};
+  }
+  return PVA_OK;
 }
 
 int need_full_queries(const pva_seg_desc* d) {
@@ -309,13 +337,13 @@ int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
                     const pva_seg_desc* seg_desc, float scale, void* out, void* stream) {
   int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  return fwd_bf16(q, k, v, cu_seqlens, cu_seqlens, seg_desc, scale, out, 0, nullptr, stream);
+  return fwd_bf16(q, k, v, cu_seqlens, cu_seqlens, seg_desc, scale, plain_out(out), stream);
 }
 
 int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
                            void* stream) {
-  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, 0, nullptr, stream);
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, plain_out(out), stream);
 }
 
 int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
@@ -323,7 +351,8 @@ int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const i
                             float* lse, void* stream) {
   if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out_f32, 1, lse, stream);
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, pva::OutSpec{out_f32, 1, lse, nullptr, nullptr},
+                  stream);
 }
 
 int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool, const int32_t* block_table,
@@ -360,7 +389,7 @@ int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
     }
   }
   const pva::PagedKV pg{block_table, table_stride, block_size, num_blocks};
-  st = pva::launch_fwd_bf16(q, k_pool, v_pool, cu_seqlens_q, seg_desc, scale, out, 0, nullptr, &pg, s);
+  st = pva::launch_fwd_bf16(q, k_pool, v_pool, cu_seqlens_q, seg_desc, scale, plain_out(out), &pg, s);
   if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
   return ok();
 }
@@ -385,15 +414,14 @@ int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float
                         void* out, void* stream) {
   int st = need_full_queries(seg_desc);
   if (st != PVA_OK) return st;
-  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, cu_seqlens, seg_desc, scale, out, 0, nullptr,
-                 stream);
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens, cu_seqlens, seg_desc, scale, plain_out(out), stream);
 }
 
 int packed_attn_fwd_varlen_fp8(const void* q, const void* k, const void* v, const float* q_scale,
                                const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                                const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
                                void* stream) {
-  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out, 0, nullptr,
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, plain_out(out),
                  stream);
 }
 
@@ -403,8 +431,27 @@ int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, con
                                 float* out_f32, float* lse, void* stream) {
   if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
-  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, out_f32, 1, lse,
-                 stream);
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale,
+                 pva::OutSpec{out_f32, 1, lse, nullptr, nullptr}, stream);
+}
+
+int packed_attn_fwd_partial_accumulate(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
+                                       const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                       float* o_acc, float* lse_acc, void* out, void* stream) {
+  pva::OutSpec spec{};
+  int st = accumulate_out(seg_desc, o_acc, lse_acc, out, &spec);
+  if (st != PVA_OK) return st;
+  return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, spec, stream);
+}
+
+int packed_attn_fwd_partial_accumulate_fp8(const void* q, const void* k, const void* v, const float* q_scale,
+                                           const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
+                                           const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
+                                           float* o_acc, float* lse_acc, void* out, void* stream) {
+  pva::OutSpec spec{};
+  int st = accumulate_out(seg_desc, o_acc, lse_acc, out, &spec);
+  if (st != PVA_OK) return st;
+  return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, spec, stream);
 }
 
 const char* pva_last_error(void) { return g_last_error.c_str(); }

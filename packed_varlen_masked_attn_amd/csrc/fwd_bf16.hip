@@ -263,8 +263,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
                                                                     const int32_t* __restrict__ cu,
                                                                     const int32_t* __restrict__ lims,
                                                                     const WorkItem* __restrict__ items, int H,
-                                                                    float scale_log2, void* __restrict__ O,
-                                                                    int out_f32, float* __restrict__ lse,
+                                                                    float scale_log2, const OutSpec& out,
                                                                     Paging pg) {
   using Kn = Kernel<D>;
   using Cfg = typename Kn::Cfg;
@@ -495,39 +494,14 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T / l (bf16, or fp32 for partial results), rows of
-  // this tile only; optionally the row's log-sum-exp of the scaled scores,
-  // ln 2 * (m + log2 l) (-inf for a row with no key in range)
+  // this tile only, folded into a running result when one is given;
+  // optionally the row's log-sum-exp of the scaled scores, ln 2 * (m + log2 l)
+  // (-inf for a row with no key in range)
   const float lt = half_swap_sum(st.l);
   const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-  if (qrow < qend) {
-    const int64_t orow = qbase + int64_t(qrow) * rs;
-    if (out_f32) {
-      float* o = static_cast<float*>(O) + orow;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * i4 + e] * inv;
-          *reinterpret_cast<f32x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
-        }
-    } else {
-      __bf16* o = static_cast<__bf16*>(O) + orow;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 w;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (__bf16)(oacc[db][4 * i4 + e] * inv);
-          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
-        }
-    }
-    if (lse && g == 0)
-      lse[int64_t(it.qo_row - it.q0 + qrow) * H + it.head] =
-          lt > 0.0f ? 0.6931471805599453f * (st.m + __log2f(lt)) : -INFINITY;
-  }
+  if (qrow < qend)
+    write_row<NDB>(out, qbase + int64_t(qrow) * rs, int64_t(it.qo_row - it.q0 + qrow) * H + it.head, g, oacc, inv,
+                   lt > 0.0f ? 0.6931471805599453f * (st.m + __log2f(lt)) : -INFINITY);
 }
 
 // Two kernels over the same body: K/V contiguous in [N, H, D], or paged.
@@ -535,21 +509,21 @@ template <int D>
 __global__ __launch_bounds__(Bf16Cfg<D>::NT, 3) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
-    float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse) {
-  fwd_bf16_body<D, false>(Q, K, V, cu, lims, items, H, scale_log2, O, out_f32, lse, Paging{nullptr, 0, 0, 0});
+    float scale_log2, OutSpec out) {
+  fwd_bf16_body<D, false>(Q, K, V, cu, lims, items, H, scale_log2, out, Paging{nullptr, 0, 0, 0});
 }
 
 template <int D>
 __global__ __launch_bounds__(Bf16Cfg<D>::NT, 3) void fwd_bf16_paged_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ lims, const WorkItem* __restrict__ items, int H,
-    float scale_log2, void* __restrict__ O, int out_f32, float* __restrict__ lse, Paging pg) {
-  fwd_bf16_body<D, true>(Q, K, V, cu, lims, items, H, scale_log2, O, out_f32, lse, pg);
+    float scale_log2, OutSpec out, Paging pg) {
+  fwd_bf16_body<D, true>(Q, K, V, cu, lims, items, H, scale_log2, out, pg);
 }
 
 template <int D>
 int launch(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d, float scale,
-           void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream) {
+           const OutSpec& out, const PagedKV* paged, hipStream_t stream) {
   using Cfg = Bf16Cfg<D>;
   const int n = static_cast<int>(d->plan.items.size());
   if (n == 0) return PVA_OK;
@@ -563,10 +537,10 @@ int launch(const void* q, const void* k, const void* v, const int32_t* cu, const
     while ((1 << shift) < paged->block_size) ++shift;
     const Paging pg{paged->table, paged->stride, shift, paged->num_blocks};
     hipLaunchKernelGGL(fwd_bf16_paged_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, qp, kp, vp, cu, d->d_lims, items,
-                       d->plan.num_heads, scale_log2, out, out_f32, lse, pg);
+                       d->plan.num_heads, scale_log2, out, pg);
   } else {
     hipLaunchKernelGGL(fwd_bf16_kernel<D>, dim3(n), dim3(Cfg::NT), 0, stream, qp, kp, vp, cu, d->d_lims, items,
-                       d->plan.num_heads, scale_log2, out, out_f32, lse);
+                       d->plan.num_heads, scale_log2, out);
   }
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;
 }
@@ -574,10 +548,10 @@ int launch(const void* q, const void* k, const void* v, const int32_t* cu, const
 }  // namespace
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
-                    float scale, void* out, int out_f32, float* lse, const PagedKV* paged, hipStream_t stream) {
+                    float scale, const OutSpec& out, const PagedKV* paged, hipStream_t stream) {
   switch (d->plan.head_dim) {
-    case 64: return launch<64>(q, k, v, cu, d, scale, out, out_f32, lse, paged, stream);
-    case 128: return launch<128>(q, k, v, cu, d, scale, out, out_f32, lse, paged, stream);
+    case 64: return launch<64>(q, k, v, cu, d, scale, out, paged, stream);
+    case 128: return launch<128>(q, k, v, cu, d, scale, out, paged, stream);
     default: return PVA_ERR_UNSUPPORTED;
   }
 }

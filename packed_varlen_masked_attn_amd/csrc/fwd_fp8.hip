@@ -301,8 +301,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
                                                          const int32_t* __restrict__ cu,
                                                          const int32_t* __restrict__ lims,
                                                          const WorkItem* __restrict__ items, int H,
-                                                         float scale_log2e, void* __restrict__ O, int out_f32,
-                                                         float* __restrict__ lse) {
+                                                         float scale_log2e, OutSpec out) {
   using Kn = Fp8Kernel;
   using Cfg = Fp8Cfg;
   constexpr int D = Cfg::D, BN = Cfg::BN, NB = Cfg::NB, NKS = Cfg::NKS, NDB = Cfg::NDB, NS = Cfg::NS;
@@ -520,47 +519,21 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   wait_vmcnt<0>();
 
   // ---- epilogue: O = O^T * v_s / l (l from the row-sum MFMA), bf16, or fp32
-  // for partial results; optionally the row's log-sum-exp of the scaled
-  // scores, ln 2 * (m + log2 l - kP8Shift) with l the sum of the weights PV applied
+  // for partial results, folded into a running result when one is given;
+  // optionally the row's log-sum-exp of the scaled scores,
+  // ln 2 * (m + log2 l - kP8Shift) with l the sum of the weights PV applied
   // (-inf for a row with no key in range)
   if (wave_active && qrow < qend) {
     const float lt = lacc[0];
-    const float inv = lt > 0.0f ? vs / lt : 0.0f;
-    const int64_t orow = qbase + int64_t(qrow) * rs;
-    if (out_f32) {
-      float* o = static_cast<float*>(O) + orow;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          f32x4 w;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) w[e2] = oacc[db][4 * i4 + e2] * inv;
-          *reinterpret_cast<f32x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
-        }
-    } else {
-      __bf16* o = static_cast<__bf16*>(O) + orow;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          bf16x4 w;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) w[e2] = (__bf16)(oacc[db][4 * i4 + e2] * inv);
-          *reinterpret_cast<bf16x4*>(o + 32 * db + 8 * i4 + 4 * g) = w;
-        }
-    }
-    if (lse && g == 0)
-      lse[int64_t(it.qo_row - it.q0 + qrow) * H + it.head] =
-          lt > 0.0f ? 0.6931471805599453f * (mb + __log2f(lt)) : -INFINITY;
+    write_row<NDB>(out, qbase + int64_t(qrow) * rs, int64_t(it.qo_row - it.q0 + qrow) * H + it.head, g, oacc,
+                   lt > 0.0f ? vs / lt : 0.0f, lt > 0.0f ? 0.6931471805599453f * (mb + __log2f(lt)) : -INFINITY);
   }
 }
 
 }  // namespace
 
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks, const float* vs,
-                   const int32_t* cu, const pva_seg_desc* d, float scale, void* out, int out_f32, float* lse,
-                   hipStream_t stream) {
+                   const int32_t* cu, const pva_seg_desc* d, float scale, const OutSpec& out, hipStream_t stream) {
   if (d->plan.head_dim != Fp8Cfg::D) return PVA_ERR_UNSUPPORTED;
   if (d->plan.tile.bm != Fp8Cfg::BM || d->plan.tile.bn != Fp8Cfg::BN) return PVA_ERR_UNSUPPORTED;
   const int n = static_cast<int>(d->plan.items.size());
@@ -568,7 +541,7 @@ int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs,
   const float scale_log2e = static_cast<float>(double(scale) * 1.4426950408889634);
   hipLaunchKernelGGL(fwd_fp8_kernel, dim3(n), dim3(Fp8Cfg::NT), 0, stream, static_cast<const uint8_t*>(q),
                      static_cast<const uint8_t*>(k), static_cast<const uint8_t*>(v), qs, ks, vs, cu, d->d_lims,
-                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2e, out, out_f32, lse);
+                     static_cast<const WorkItem*>(d->d_items), d->plan.num_heads, scale_log2e, out);
   return hipGetLastError() == hipSuccess ? PVA_OK : PVA_ERR_HIP;
 }
 

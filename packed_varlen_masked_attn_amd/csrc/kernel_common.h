@@ -112,4 +112,63 @@ struct BufLoader {
   }
 };
 
+// Epilogue of one query row: the lane holds elements 32 db + 8 i4 + 4 g + e
+// (db < NDB, i4 < 4, e < 4) of the row's unnormalised O^T; inv = scale / l
+// (0 for a row with no key), lse_c the row's log-sum-exp (natural log, -inf
+// for no key). With a running result (out.acc_o), the two combine as two key
+// sets of one softmax ("[RFC]: HunyuanImage 3.0 deployment", Proposed Change
+// P2, Ring-Attention Integration): lse = log(e^lse_acc + e^lse_c),
+// O = e^(lse_acc - lse) O_acc + e^(lse_c - lse) O_c. Rows of o and lse are
+// orow (element offset of the row's first element) and lrow (row * H + head).
+template <int NDB>
+__device__ __forceinline__ void write_row(const OutSpec& out, int64_t orow, int64_t lrow, int g,
+                                          const f32x16 (&oacc)[NDB], float inv, float lse_c) {
+  // element value(col, O element) of the lane's 16-byte groups, stored as
+  // fp32 or bf16
+  auto store = [&](auto value) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int col = 32 * db + 8 * i4 + 4 * g;
+        f32x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * i4 + e];
+        w = value(col, w);
+        if (out.o_f32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(out.o) + orow + col) = w;
+        } else {
+          bf16x4 b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = (__bf16)w[e];
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(out.o) + orow + col) = b;
+        }
+      }
+  };
+  if (!out.acc_o) {
+    store([&](int, f32x4 w) { return w * inv; });
+    if (out.lse && g == 0) out.lse[lrow] = lse_c;
+    return;
+  }
+  constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  const float lp = out.acc_lse[lrow];
+  const float mx = __builtin_elementwise_maximum(lp, lse_c);
+  float wc = 0.0f, wp = 0.0f, lse_out = -INFINITY;
+  if (mx > -INFINITY) {
+    const float ep = fast_exp2((lp - mx) * kLog2e), ec = fast_exp2((lse_c - mx) * kLog2e);
+    const float sum = ep + ec, rs = 1.0f / sum;
+    wp = ep * rs;
+    wc = inv * (ec * rs);
+    lse_out = mx + kLn2 * __log2f(sum);
+  }
+  // (a row the running result has not reached reads nothing from acc_o,
+  // whatever it holds)
+  const float* po = wp > 0.0f ? out.acc_o + orow : nullptr;
+  store([&](int col, f32x4 w) {
+    const f32x4 prev = po ? *reinterpret_cast<const f32x4*>(po + col) : f32x4{};
+    return w * wc + prev * wp;
+  });
+  if (out.lse && g == 0) out.lse[lrow] = lse_out;
+}
+
 }  // namespace pva

@@ -95,6 +95,23 @@ struct Plan {
   }
 };
 
+// Where a forward launch writes its result (device pointers). Rows are the
+// queried rows in packed order; lse is indexed row * H + head.
+//   o        bf16 [rows, H, D], or fp32 when o_f32
+//   lse      fp32 log-sum-exp of each row's scaled scores, or null
+//   acc_o,   a running fp32 result [rows, H, D] and its log-sum-exp over other
+//   acc_lse  keys of the same rows, folded into this launch's result before it
+//            is written (log-sum-exp weights; a row whose acc_lse is -inf
+//            takes nothing from acc_o), or both null. o and lse may be acc_o
+//            and acc_lse: each lane reads its elements before writing them.
+struct OutSpec {
+  void* o;
+  int o_f32;
+  float* lse;
+  const float* acc_o;
+  const float* acc_lse;
+};
+
 // K / V held in a paged pool [num_blocks, block_size, H, D] (device table).
 struct PagedKV {
   const int32_t* table;  // device int32 [nseq * stride]: pool block of each block of keys

@@ -26,8 +26,8 @@
 // This build holds no kernels: the C-ABI layer's launchers are stand-ins
 // that must never be reached (every call here fails validation on the host).
 namespace pva {
-int launch_fwd_bf16(const void*, const void*, const void*, const int32_t*, const pva_seg_desc*, float, void*, int,
-                    float*, const PagedKV*, hipStream_t) {
+int launch_fwd_bf16(const void*, const void*, const void*, const int32_t*, const pva_seg_desc*, float, const OutSpec&,
+                    const PagedKV*, hipStream_t) {
   std::fprintf(stderr, "FAIL: a bf16 launch was reached\n");
   std::abort();
 }
@@ -36,7 +36,7 @@ int launch_merge(const float*, const float*, int, int64_t, int, void*, float*, h
   std::abort();
 }
 int launch_fwd_fp8(const void*, const void*, const void*, const float*, const float*, const float*, const int32_t*,
-                   const pva_seg_desc*, float, void*, int, float*, hipStream_t) {
+                   const pva_seg_desc*, float, const OutSpec&, hipStream_t) {
   std::fprintf(stderr, "FAIL: an fp8 launch was reached\n");
   std::abort();
 }
