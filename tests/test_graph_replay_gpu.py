@@ -140,3 +140,50 @@ def test_partials_and_merge_graph():
         return [o, ls]
 
     _replays(lambda: calls(o_parts, l_parts, out, lse), [q] + kp + vp, fresh, [out, lse], eager)
+
+
+def test_chunks_folded_into_a_running_result_graph():
+    """packed_attn_fwd_partial for the first key chunk, then
+    packed_attn_fwd_partial_accumulate for the second into the bf16 output:
+    the running buffers are rewritten by the first call of every replay."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    D, H = 128, 2
+    t, i = (100, 100, 30, 30), (500, 500, 200, 200)
+    w = workloads.custom(t, i, H, D, seed=7400)
+    seqs = [([a, b], [0, 1]) for a, b in zip(t, i)]
+    L = [a + b for a, b in zip(t, i)]
+    q, k, v = (x.cuda() for x in workloads.bf16_inputs(w))
+    off = np.cumsum([0] + L)
+    parts = []
+    for p in range(2):
+        lo = [n * p // 2 for n in L]
+        hi = [n * (p + 1) // 2 for n in L]
+        d = pva.SegDesc.segments(seqs, H, D, "bf16", k_lo=lo, k_hi=hi)
+        idx = torch.from_numpy(np.concatenate([np.arange(off[s] + a, off[s] + b) for s, (a, b) in
+                                               enumerate(zip(lo, hi))])).cuda()
+        parts.append((d, idx, torch.from_numpy(d.cu_seqlens).cuda()))
+    cuq = torch.from_numpy(parts[0][0].cu_seqlens_q).cuda()
+    kp = [k.index_select(0, idx).contiguous() for _, idx, _ in parts]
+    vp = [v.index_select(0, idx).contiguous() for _, idx, _ in parts]
+    N = sum(L)
+    o_acc = torch.empty((N, H, D), dtype=torch.float32, device="cuda")
+    l_acc = torch.empty((N, H), dtype=torch.float32, device="cuda")
+    out = torch.empty((N, H, D), dtype=torch.bfloat16, device="cuda")
+    scale = 1 / math.sqrt(D)
+    gen = torch.Generator(device="cuda").manual_seed(7401)
+
+    def calls(oa, la, o):
+        (d0, _, cuk0), (d1, _, cuk1) = parts
+        pva.packed_attn_fwd_partial(q, kp[0], vp[0], cuq, cuk0, d0, scale, oa, la)
+        pva.packed_attn_fwd_partial_accumulate(q, kp[1], vp[1], cuq, cuk1, d1, scale, oa, la, o)
+
+    def fresh(i):
+        return [torch.randn(x.shape, generator=gen, device="cuda").to(torch.bfloat16) for x in [q] + kp + vp]
+
+    def eager():
+        oa, la, o = torch.empty_like(o_acc), torch.empty_like(l_acc), torch.empty_like(out)
+        calls(oa, la, o)
+        return [o, la]
+
+    _replays(lambda: calls(o_acc, l_acc, out), [q] + kp + vp, fresh, [out, l_acc], eager)
