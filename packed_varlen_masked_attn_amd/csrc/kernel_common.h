@@ -123,8 +123,8 @@ struct BufLoader {
 template <int NDB>
 __device__ __forceinline__ void write_row(const OutSpec& out, int64_t orow, int64_t lrow, int g,
                                           const f32x16 (&oacc)[NDB], float inv, float lse_c) {
-  // element value(col, O element) of the lane's 16-byte groups, stored as
-  // fp32 or bf16
+  // value(group, O elements) of the lane's 4-element groups (group
+  // 4 db + i4 holds columns 32 db + 8 i4 + 4 g .. +3), stored as fp32 or bf16
   auto store = [&](auto value) {
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -134,7 +134,7 @@ __device__ __forceinline__ void write_row(const OutSpec& out, int64_t orow, int6
         f32x4 w;
 #pragma unroll
         for (int e = 0; e < 4; ++e) w[e] = oacc[db][4 * i4 + e];
-        w = value(col, w);
+        w = value(4 * db + i4, w);
         if (out.o_f32) {
           *reinterpret_cast<f32x4*>(static_cast<float*>(out.o) + orow + col) = w;
         } else {
@@ -151,7 +151,15 @@ __device__ __forceinline__ void write_row(const OutSpec& out, int64_t orow, int6
     return;
   }
   constexpr float kLog2e = 1.4426950408889634f, kLn2 = 0.6931471805599453f;
+  // the running row and its log-sum-exp are read together (one memory round
+  // trip); the row is used only where the log-sum-exp says it holds a result
   const float lp = out.acc_lse[lrow];
+  f32x4 prev[NDB * 4];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4)
+      prev[4 * db + i4] = *reinterpret_cast<const f32x4*>(out.acc_o + orow + 32 * db + 8 * i4 + 4 * g);
   const float mx = __builtin_elementwise_maximum(lp, lse_c);
   float wc = 0.0f, wp = 0.0f, lse_out = -INFINITY;
   if (mx > -INFINITY) {
@@ -161,13 +169,10 @@ __device__ __forceinline__ void write_row(const OutSpec& out, int64_t orow, int6
     wc = inv * (ec * rs);
     lse_out = mx + kLn2 * __log2f(sum);
   }
-  // (a row the running result has not reached reads nothing from acc_o,
-  // whatever it holds)
-  const float* po = wp > 0.0f ? out.acc_o + orow : nullptr;
-  store([&](int col, f32x4 w) {
-    const f32x4 prev = po ? *reinterpret_cast<const f32x4*>(po + col) : f32x4{};
-    return w * wc + prev * wp;
-  });
+  // (a row the running result has not reached takes nothing from acc_o,
+  // whatever it holds: NaN there must not reach the result)
+  const bool use_prev = wp > 0.0f;
+  store([&](int grp, f32x4 w) { return w * wc + (use_prev ? prev[grp] * wp : f32x4{}); });
   if (out.lse && g == 0) out.lse[lrow] = lse_out;
 }
 
