@@ -212,13 +212,14 @@ int accumulate_out(const pva_seg_desc* d, float* o_acc, float* lse_acc, void* ou
   if (!aligned16(o_acc)) return set_error(PVA_ERR_INVALID_ARG, "o_acc must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(lse_acc) & 3u) != 0)
     return set_error(PVA_ERR_INVALID_ARG, "lse_acc must be 4-byte aligned");
+  // other rows' running values must not be overwritten before they are read
+  const uintptr_t elems = uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads) * uintptr_t(d->plan.head_dim);
+  const uintptr_t b0 = reinterpret_cast<uintptr_t>(o_acc), b1 = b0 + 4 * elems;
+  const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse_acc),
+                  l1 = l0 + 4 * uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads);
+  if (b0 < l1 && l0 < b1) return set_error(PVA_ERR_INVALID_ARG, "o_acc overlaps lse_acc");
   if (out) {
-    // other rows' running values must not be overwritten before they are read
-    const uintptr_t elems = uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads) * uintptr_t(d->plan.head_dim);
     const uintptr_t a0 = reinterpret_cast<uintptr_t>(out), a1 = a0 + 2 * elems;
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(o_acc), b1 = b0 + 4 * elems;
-    const uintptr_t l0 = reinterpret_cast<uintptr_t>(lse_acc),
-                    l1 = l0 + 4 * uintptr_t(d->plan.total_q) * uintptr_t(d->plan.num_heads);
     if ((a0 < b1 && b0 < a1) || (a0 < l1 && l0 < a1))
       return set_error(PVA_ERR_INVALID_ARG, "out overlaps o_acc or lse_acc");
     *spec = pva::OutSpec{out, 0, lse_acc, o_acc, lse_acc};

@@ -364,13 +364,18 @@ void reject_cases() {
              PVA_ERR_INVALID_ARG, "accumulate without lse_acc");
   expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, fb + 1, fb, nullptr, nullptr) ==
              PVA_ERR_INVALID_ARG, "misaligned o_acc");
-  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, fb, fb, buf + 16, nullptr) ==
-             PVA_ERR_INVALID_ARG, "bf16 output overlapping the running buffers");
+  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, fb, fb + 4, nullptr, nullptr) ==
+             PVA_ERR_INVALID_ARG, "o_acc overlapping lse_acc");
+  alignas(16) static float o_run[4096], l_run[64];  // one row set: 12 rows x 2 heads x 64
+  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, o_run, l_run, o_run + 8, nullptr) ==
+             PVA_ERR_INVALID_ARG, "bf16 output overlapping o_acc");
+  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, o_run, l_run, l_run, nullptr) ==
+             PVA_ERR_INVALID_ARG, "bf16 output overlapping lse_acc");
   expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, nullptr, 0.1f, fb, fb, nullptr, nullptr) ==
              PVA_ERR_INVALID_ARG, "accumulate NULL desc");
-  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, fb, fb, nullptr, nullptr) ==
+  expect(packed_attn_fwd_partial_accumulate(buf, buf, buf, cu, cu, h.d, 0.1f, o_run, l_run, nullptr, nullptr) ==
              PVA_ERR_INVALID_ARG, "accumulate on a host-only descriptor");
-  expect(packed_attn_fwd_partial_accumulate_fp8(buf, buf, buf, fb, fb, fb, cu, cu, h.d, 0.1f, fb, fb, nullptr,
+  expect(packed_attn_fwd_partial_accumulate_fp8(buf, buf, buf, fb, fb, fb, cu, cu, h.d, 0.1f, o_run, l_run, nullptr,
                                                 nullptr) == PVA_ERR_INVALID_ARG, "fp8 accumulate on a bf16 descriptor");
   expect(pva_merge_partials(nullptr, nullptr, 1, 4, 64, buf, nullptr, nullptr) == PVA_ERR_INVALID_ARG, "merge NULL");
   expect(pva_merge_partials(reinterpret_cast<float*>(buf), reinterpret_cast<float*>(buf), 0, 4, 64, buf, nullptr,
