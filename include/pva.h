@@ -318,14 +318,16 @@ int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, con
  *   O   = exp(lse_acc - lse) O_acc + exp(lse_c - lse) O_c.
  *   o_acc   : device float [total_q, H, D], 16-byte aligned: the running O
  *             (from packed_attn_fwd_partial or an earlier call of this one)
- *   lse_acc : device float [total_q, H], 4-byte aligned: its log-sum-exp;
- *             -inf marks a row no chunk has given a key yet, whose o_acc row
- *             is then not read (it may hold anything)
+ *   lse_acc : device float [total_q, H], 4-byte aligned, disjoint from
+ *             o_acc: its log-sum-exp; -inf marks a row no chunk has given a
+ *             key yet, whose o_acc row then does not enter the result (it
+ *             may hold anything, NaN included)
  *   out     : NULL: the merged O goes back to o_acc; else device bf16
  *             [total_q, H, D], 16-byte aligned, disjoint from o_acc and
  *             lse_acc: the merged O goes there in bf16 (the last chunk) and
  *             o_acc is left as it was
- * lse_acc receives the merged log-sum-exp in both cases. Starting from
+ * lse_acc receives the merged log-sum-exp in both cases. Overlapping
+ * buffers are refused (PVA_ERR_INVALID_ARG) before anything is launched. Starting from
  * lse_acc = -inf everywhere, one call per chunk gives the result of
  * packed_attn_fwd_partial + pva_merge_partials without the per-chunk fp32
  * outputs and the merge pass. Calls on one o_acc must be ordered (one
