@@ -462,7 +462,11 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     // S(j+1) MFMAs beside the exponentials of tile j
     i32x8 pb;
     float pf[NB * 16];
+    // (raised wave priority: while one wave of the SIMD works through this
+    // VALU-heavy phase, the other's PV MFMAs fill the matrix pipe)
+    __builtin_amdgcn_s_setprio(1);
     Kn::s_with_probs(snext, kst[(SJ + 1) % NS], qf, scur, scale_log2, mb, pb, pf, kad);
+    __builtin_amdgcn_s_setprio(0);
     if (__builtin_expect(k1 + BN > wlim_min, 0)) Kn::mask(snext, k1, g, mylim);
     // PV(j) MFMAs beside the row max of tile j+1
     const float mt = Kn::pv_with_max(oacc, lacc, vst[SJ], pb, sel, snext, vrow0, vsw, half, p8);
