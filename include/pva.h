@@ -327,11 +327,12 @@ int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, con
  *             lse_acc: the merged O goes there in bf16 (the last chunk) and
  *             o_acc is left as it was
  * lse_acc receives the merged log-sum-exp in both cases. Overlapping
- * buffers are refused (PVA_ERR_INVALID_ARG) before anything is launched. Starting from
- * lse_acc = -inf everywhere, one call per chunk gives the result of
- * packed_attn_fwd_partial + pva_merge_partials without the per-chunk fp32
- * outputs and the merge pass. Calls on one o_acc must be ordered (one
- * stream). Other arguments and errors as packed_attn_fwd_partial.
+ * buffers are refused (PVA_ERR_INVALID_ARG) before anything is launched.
+ * Starting from lse_acc = -inf everywhere, one call per chunk gives the
+ * result of packed_attn_fwd_partial + pva_merge_partials without the
+ * per-chunk fp32 outputs and the merge pass. Calls on one o_acc must be
+ * ordered (one stream). Other arguments and errors as
+ * packed_attn_fwd_partial.
  */
 int packed_attn_fwd_partial_accumulate(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                                        const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
