@@ -91,3 +91,63 @@ def test_fp8_many_sequences():
     t = (1, 1, 0, 0, 63, 63) + t
     i = (0, 0, 1, 1, 65, 65) + i
     _full(workloads.custom(t, i, 2, 128, seed=6400, dtype="fp8"), "many sequences")
+
+
+def _fp8_launch(w, codes, scales):
+    """One fp8 launch on given E4M3 codes (uint8 [N, H, D]) and per-(sequence,
+    head) scales; returns the bf16 output on the host."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    desc = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, "fp8")
+    cu = torch.from_numpy(desc.cu_seqlens).cuda()
+    q, k, v = (c.cuda() for c in codes)
+    sc = [torch.from_numpy(np.ascontiguousarray(s)).cuda() for s in scales]
+    out = torch.empty((w.total_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
+    pva.packed_attn_fwd_fp8(q, k, v, *sc, cu, desc, 1.0 / math.sqrt(w.head_dim), out)
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+def test_fp8_text_rows_ignore_image_tokens():
+    """With the codes of every image token replaced (scales held fixed), the
+    text rows' outputs are bitwise unchanged: a text row never reads an image
+    key or value."""
+    import torch
+    w = workloads.custom([250, 37], [600, 300], 3, 128, seed=6500, dtype="fp8")
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    codes = [x.view(torch.uint8).clone() for x in (q8, k8, v8)]
+    out1 = _fp8_launch(w, codes, (qs, ks, vs))
+    off = oracle.offsets(w.seq_len)
+    g = torch.Generator().manual_seed(6501)
+    codes2 = [c.clone() for c in codes]
+    for s in range(w.nseq):
+        a, b = off[s] + w.text_len[s], off[s + 1]
+        for c in codes2:
+            new = torch.randint(0, 256, c[a:b].shape, generator=g, dtype=torch.uint8)
+            new[(new & 0x7F) == 0x7F] = 0x38  # no NaN codes (0x7F / 0xFF): E4M3 1.0 instead
+            c[a:b] = new
+    out2 = _fp8_launch(w, codes2, (qs, ks, vs))
+    say("[fp8] text rows ignore image tokens")
+    for s in range(w.nseq):
+        a = off[s]
+        assert torch.equal(out1[a:a + w.text_len[s]], out2[a:a + w.text_len[s]])
+    assert not torch.equal(out1, out2)  # the image rows did change
+
+
+def test_fp8_pack_order_invariance():
+    """Sequences reordered with their codes and scales: every row's output is
+    bitwise the same (one work item per row, fixed key order)."""
+    import torch
+    w = workloads.custom([100, 5, 260], [300, 700, 0], 2, 128, seed=6600, dtype="fp8")
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    codes = [x.view(torch.uint8) for x in (q8, k8, v8)]
+    out1 = _fp8_launch(w, codes, (qs, ks, vs))
+    order = [2, 0, 1]
+    off = oracle.offsets(w.seq_len)
+    idx = torch.cat([torch.arange(off[s], off[s + 1]) for s in order])
+    w2 = workloads.custom([w.text_len[s] for s in order], [w.image_len[s] for s in order], 2, 128, seed=6600,
+                          dtype="fp8")
+    # scales are [nseq, H]: reorder their sequences the same way
+    out2 = _fp8_launch(w2, [c[idx] for c in codes], [x[order] for x in (qs, ks, vs)])
+    say("[fp8] pack order")
+    assert torch.equal(out1[idx], out2)
