@@ -219,3 +219,45 @@ def test_accumulate_rejects_overlapping_output():
                                                     vp(lse_acc.data_ptr()), vp(bad), None)
         assert st == pva.PVA_ERR_INVALID_ARG
         assert "overlaps" in lib.pva_last_error().decode()
+
+
+def test_accumulate_guard_bands():
+    """The running O, its log-sum-exp and the bf16 output, each a view into
+    the middle of a larger buffer: the guard rows on either side stay as
+    they were through a partial launch and two accumulating ones."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    seqs = [oracle.make_seq([45, 190], [oracle.CAUSAL, oracle.FULL]),
+            oracle.make_seq([130, 70], [oracle.CAUSAL, oracle.FULL])]
+    H, D = 2, 128
+    qc, kc, vc = _inputs(seqs, H, D, 170)
+    N = sum(s.length for s in seqs)
+    G = 8
+    ob = torch.full((N + 2 * G, H, D), 777.0, dtype=torch.float32, device="cuda")
+    lb = torch.full((N + 2 * G, H), 777.0, dtype=torch.float32, device="cuda")
+    bb = torch.full((N + 2 * G, H, D), 777.0, dtype=torch.bfloat16, device="cuda")
+    o_acc, lse_acc, out = ob[G:G + N], lb[G:G + N], bb[G:G + N]
+    before = [buf.cpu().clone() for buf in (ob, lb, bb)]  # (777 is 776 in bf16)
+    q = qc.cuda()
+    cuts = [(0, s.length // 3, 2 * s.length // 3, s.length) for s in seqs]
+    for p in range(3):
+        lo = [c[p] for c in cuts]
+        hi = [c[p + 1] for c in cuts]
+        desc = _desc(seqs, H, D, lo, hi)
+        k = _chunk_rows(kc, seqs, lo, hi).cuda()
+        v = _chunk_rows(vc, seqs, lo, hi).cuda()
+        cuq = torch.from_numpy(desc.cu_seqlens_q).cuda()
+        cuk = torch.from_numpy(desc.cu_seqlens).cuda()
+        if p == 0:
+            pva.packed_attn_fwd_partial(q, k, v, cuq, cuk, desc, 1 / math.sqrt(D), o_acc, lse_acc)
+        else:
+            pva.packed_attn_fwd_partial_accumulate(q, k, v, cuq, cuk, desc, 1 / math.sqrt(D), o_acc, lse_acc,
+                                                   out if p == 2 else None)
+    torch.cuda.synchronize()
+    for buf, b0 in zip((ob, lb, bb), before):
+        b = buf.cpu()
+        assert torch.equal(b[:G], b0[:G]) and torch.equal(b[G + N:], b0[G + N:])
+    full = oracle.segment_attention(f64(qc), f64(kc), f64(vc), seqs, 1 / math.sqrt(D))
+    mx, mean = err_stats(f64(out), full)
+    say(f"[accumulate] guard bands: max {mx:.3e}")
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
