@@ -603,6 +603,7 @@ def main():
     if w.name == "mixed_res_cfg_batch" and not args.no_other_configs:
         result["other_configs"] = {key: config_record(key, args.other_steps, max(5, args.warmup))
                                    for key in ("mixed_res_fp8", "single_1024", "sp4_share")}
+        result["next_rows"] = next_rows(args.other_steps)
 
     padded_out = None
     if not args.no_padded and not is_fp8 and not segmented:
@@ -693,6 +694,49 @@ def config_record(key, steps, warmup):
     del q, k, v, out
     torch.cuda.empty_cache()
     return rec
+
+
+# The rows built past the hot path, each timed by its own bench.py run
+# (kernel-only unless noted): Prefix-KV queries, multi-segment masks, key
+# chunks (partials + merge, and folded into a running result), paged K/V.
+NEXT_ROWS = {
+    "prefix_kv": ["--workload", "mixed_res_prefix", "--kernel-only"],
+    "prefix_kv_fp8": ["--workload", "mixed_res_prefix_fp8", "--kernel-only"],
+    "segments": ["--workload", "edit_segments", "--kernel-only"],
+    "segments_fp8": ["--workload", "edit_segments_fp8", "--kernel-only"],
+    "key_chunks_2": ["--workload", "mixed_res", "--split-keys", "2"],
+    "key_chunks_2_fused": ["--workload", "mixed_res", "--split-keys", "2", "--fused"],
+    "key_chunks_2_fp8_fused": ["--workload", "mixed_res_fp8", "--split-keys", "2", "--fused"],
+    "paged_256": ["--workload", "mixed_res_prefix", "--paged", "256", "--kernel-only"],
+}
+
+
+def next_rows(steps):
+    """Runs each NEXT_ROWS configuration in a child bench.py process (its
+    own inputs and device memory) and keeps the figures of its JSON line."""
+    import subprocess
+    recs = {}
+    for name, extra in NEXT_ROWS.items():
+        cmd = [sys.executable, os.path.abspath(__file__), *extra, "--steps", str(steps), "--warmup", "5",
+               "--no-other-configs", "--no-cpu", "--no-padded", "--cold-iters", "0"]
+        t0 = time.time()
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=300)
+        lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+        if r.returncode != 0 or not lines:
+            recs[name] = {"error": f"exit {r.returncode}", "stderr_tail": r.stderr[-400:]}
+            log(f"[bench] next row {name}: failed (exit {r.returncode})")
+            continue
+        j = json.loads(lines[-1])
+        rec = {"workload": j["config"]["workload"], "dtype": j["dtype"], "ms_per_step": j["ms_per_step"],
+               "useful_tflops_per_step": j["value"], "roofline": j.get("roofline")}
+        for key in ("kernel_ms", "partials_ms", "merge_ms", "launches_ms"):
+            if key in j:
+                rec[key] = j[key]
+        rec["config"] = {k: v for k, v in j["config"].items() if k in ("split_keys", "fused", "paged_block_rows")}
+        recs[name] = rec
+        log(f"[bench] next row {name}: {j['ms_per_step']:.4f} ms/step -> {j['value']:.1f} useful TFLOP/s "
+            f"({time.time() - t0:.1f}s)")
+    return recs
 
 
 def split_keys_bench(args, w, q, k, v, scale, flops, desc_us, fp8_scales=None):

@@ -177,3 +177,15 @@ def test_padded_batch_matches_the_oracle_padding():
     for x, xp in ((q, qp), (k, kp), (v, vp)):
         assert np.array_equal(xp.float().numpy().astype(np.float64), oracle.padded_layout(x.float().numpy(), w.seq_len))
     assert torch.equal(bench.unpad(qp, w), q)
+
+
+def test_next_row_arguments_parse(monkeypatch):
+    """Every configuration the bench line's next_rows runs is a valid
+    bench.py command line (a typo would only show as a failed row)."""
+    import workloads
+    for name, extra in bench.NEXT_ROWS.items():
+        monkeypatch.setattr(sys, "argv", ["bench.py", *extra, "--steps", "5", "--warmup", "5", "--no-other-configs",
+                                          "--no-cpu", "--no-padded", "--cold-iters", "0"])
+        a = bench.parse()
+        assert a.workload in workloads.WORKLOADS, name
+        assert a.kernel_only or a.split_keys > 1, name
