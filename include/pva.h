@@ -87,7 +87,7 @@ typedef struct pva_seg_desc pva_seg_desc;
  *   text_len, image_len : host int32 [nseq], copied; T >= 0, I >= 0, T+I >= 1
  *   nseq                : >= 1, sum of lengths must fit in int32
  *   num_heads           : H >= 1, H * head_dim * N must fit in int64
- *   head_dim            : D in {64, 128}
+ *   head_dim            : D in {64, 128} for PVA_BF16, 128 for PVA_FP8_E4M3
  *                         (every sequence needs L * H * D * e < 2^31, e = 2
  *                         bytes per bf16 element, 1 per fp8 code: one head's
  *                         rows are addressed with 32-bit byte offsets;
