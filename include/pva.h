@@ -28,8 +28,10 @@
  * pva_seg_desc_build_kv_chunk, K and V may hold just a chunk of each
  * sequence's keys; packed_attn_fwd_partial (bf16) or
  * packed_attn_fwd_partial_fp8 then also returns the rows' log-sum-exp and
- * pva_merge_partials combines the chunks' results. packed_attn_fwd_paged
- * reads K and V from a block pool through a block table.
+ * pva_merge_partials combines the chunks' results, or
+ * packed_attn_fwd_partial_accumulate(_fp8) folds each chunk into a running
+ * result as it is computed. packed_attn_fwd_paged reads K and V from a block
+ * pool through a block table.
  *
  * Ownership: the caller owns every tensor and every stream. The library owns
  * only a pva_seg_desc (host copy + device work list), freed by
