@@ -224,7 +224,8 @@ int pva_seg_desc_tile(const pva_seg_desc* desc, int32_t* block_m, int32_t* block
  * {seq, head, q0, q_rows, k_full_end, k_end, qo_row, L}: query rows
  * [q0, q0 + q_rows) of sequence seq (row numbers within the sequence), key
  * tiles below k_full_end need no mask, tiles from k_end on are skipped,
- * qo_row is the Q/O row holding query row q0, L the sequence length;
+ * qo_row is the Q/O row holding query row q0, L the K/V rows k and v hold
+ * for the sequence (its length; the chunk's rows for a key-chunk descriptor);
  * seq = -1 marks an empty slot that keeps the XCD alignment of the list.
  * Valid until freed. */
 int pva_seg_desc_work_items(const pva_seg_desc* desc, const int32_t** items, int32_t* n_items);
