@@ -88,6 +88,10 @@ def parse():
                     help="summarise a rocprofv3 counter file of a --kernel-only run (MFMA busy and co-issue "
                          "cycles, LDS bank conflicts, L2 hits, instruction counts) and one of the derived "
                          "MfmaUtil counter (no GPU needed); prints the counter record for --workload")
+    ap.add_argument("--timeline", action="store_true",
+                    help="run the workload on libpva_timeline.so (the library with the per-workgroup timeline "
+                         "compiled in) and print the timeline summary of the median of three recorded launches "
+                         "instead of the bench line")
     ap.add_argument("--stall-summary", nargs=2, metavar=("WAVE_CSV", "ISSUE_CSV"),
                     help="summarise two rocprofv3 counter files of --kernel-only runs: wave states (resident, "
                          "waiting, issuing) and the MFMA pipe's busy cycles with the shader clock (no GPU needed); "
@@ -344,6 +348,118 @@ def stored_counters(dtype, workload):
     return ctr
 
 
+# workgroup-timeline record fields (include/pva.h, pva_timeline_read)
+TL_T0, TL_T1, TL_T2, TL_T3, TL_C1, TL_C2, TL_HWID, TL_XCC, TL_TILES, TL_KEND, TL_WG, TL_OK = range(12)
+TL_NS_PER_TICK = 10.0  # the real-time counter runs at 100 MHz
+
+
+def timeline_summary(records, n_slots):
+    """Key/value lines summarising one launch's workgroup timeline: records
+    uint64 [n, 12] (pva_timeline_read); n_slots workgroup slots of the chip
+    (CUs x workgroups per CU). Times in microseconds from the first start."""
+    rec = np.asarray(records)
+    rec = rec[rec[:, TL_OK] == 1].astype(np.int64)
+    if len(rec) == 0:
+        return ["records: 0"]
+    t = {i: (rec[:, i] - rec[:, TL_T0].min()) * TL_NS_PER_TICK for i in (TL_T0, TL_T1, TL_T2, TL_T3)}
+    t0, t1, t2, t3 = t[TL_T0], t[TL_T1], t[TL_T2], t[TL_T3]
+    cyc = (rec[:, TL_C2] - rec[:, TL_C1]).astype(np.float64)
+    tiles = rec[:, TL_TILES]
+    hw, xcc = rec[:, TL_HWID], rec[:, TL_XCC] & 0xF
+    cu = ((hw >> 8) & 0xF) | (((hw >> 12) & 1) << 4) | (((hw >> 13) & 0x7) << 5) | (xcc << 8)
+    span = float(t3.max())
+    loop = t2 - t1
+    busy = tiles > 0
+    per_tile_ns = loop[busy] / tiles[busy]
+    per_tile_cyc = cyc[busy] / tiles[busy]
+    clock = cyc / np.maximum(loop, 1.0)  # cycles per ns = GHz
+    long_loop = loop > 20000.0  # clocks only from loops of 20 us or more
+    # share of each CU's time with k workgroups inside their tile loop, and the
+    # gap between a workgroup's end and the next start on the same CU
+    share = np.zeros(5)
+    gaps = []
+    for c in np.unique(cu):
+        m = cu == c
+        ev = sorted([(a, 1) for a in t1[m]] + [(b, -1) for b in t2[m]])
+        cur, prev = 0, 0.0
+        for when, d in ev:
+            share[min(cur, 4)] += when - prev
+            cur += d
+            prev = when
+        share[0] += span - prev
+        ends = np.sort(t3[m])
+        for start in np.sort(t0[m]):
+            before = ends[ends <= start]
+            if len(before):
+                gaps.append(start - before[-1])
+    share /= share.sum()
+    lines = [
+        f"records: {len(rec)}",
+        f"cus: {len(np.unique(cu))}",
+        f"span_us: {span / 1e3:.1f}",
+        f"ideal_span_us_at_median_tile: {np.median(per_tile_ns) * tiles.sum() / n_slots / 1e3 if busy.any() else 0.0:.1f}",
+        f"tiles_per_item_mean: {tiles.mean():.1f}",
+        f"per_tile_ns_median: {np.median(per_tile_ns) if busy.any() else 0.0:.0f}",
+        f"per_tile_shader_cycles_median: {np.median(per_tile_cyc) if busy.any() else 0.0:.0f}",
+        f"prologue_us_median: {np.median(t1 - t0) / 1e3:.2f}",
+        f"epilogue_us_median: {np.median(t3 - t2) / 1e3:.2f}",
+        f"refill_gap_us_median: {(np.median(gaps) / 1e3) if gaps else 0.0:.2f}",
+        "cu_time_pct_with_k_computing_workgroups: " + " ".join(f"{k}:{100 * share[k]:.1f}" for k in range(5)),
+        f"shader_clock_ghz_median: {np.median(clock[long_loop]) if long_loop.any() else 0.0:.3f}",
+    ]
+    xl = []
+    for x in range(8):
+        m = xcc == x
+        if not m.any():
+            continue
+        mc = m & long_loop
+        xl.append(f"{x}:{np.median(clock[mc]) if mc.any() else 0.0:.3f}GHz/"
+                  f"{np.median(per_tile_ns[m[busy]]) if (m & busy).any() else 0.0:.0f}ns/{t3[m].max() / 1e3:.0f}us")
+    lines.append("per_xcd_clock_tile_end: " + " ".join(xl))
+    ql = []
+    for a, b in ((0, .25), (.25, .5), (.5, .75), (.75, .9), (.9, 1.01)):
+        m = long_loop & (t2 >= a * span) & (t2 < b * span)
+        if m.any():
+            ql.append(f"[{a:.2f},{min(b, 1):.2f}):{np.median(clock[m]):.3f}")
+    lines.append("shader_clock_ghz_by_loop_end_in_launch: " + " ".join(ql))
+    return lines
+
+
+def timeline_run(desc, step, dtype, workload_arg, workload_name, workgroups_per_cu):
+    """Three recorded launches on the timeline build; prints the summary of
+    the one with the median span."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    n = len(desc.work_items)
+    if n > pva.binding.TIMELINE_MAX_ITEMS:
+        sys.exit(f"--timeline records at most {pva.binding.TIMELINE_MAX_ITEMS} work items ({n} here)")
+    runs = []
+    for _ in range(3):
+        pva.timeline_clear(dtype)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        recs = pva.timeline_read(dtype, n)
+        written = recs[recs[:, TL_OK] == 1].astype(np.int64)
+        span = (written[:, TL_T3].max() - written[:, TL_T0].min()) * TL_NS_PER_TICK / 1e3
+        runs.append((span, a.elapsed_time(b), recs))
+        log(f"[timeline] launch: {a.elapsed_time(b):.4f} ms (event), span {span:.1f} us")
+    runs.sort(key=lambda r: r[0])
+    span, ms, recs = runs[1]
+    kernel = "fwd_fp8_kernel" if dtype == "fp8" else "fwd_bf16_kernel"
+    print(f"# Workgroup timeline of {kernel} on the {workload_name} workload (MI355X, libpva_timeline.so: the "
+          "library with per-work-item s_memrealtime / s_memtime stamps compiled in)")
+    print(f"# command (from the repository root): python -u bench.py --workload {workload_arg} --timeline")
+    print("# the median-span launch of three; per-tile figures over the first wave's key tiles; clocks from "
+          "loops of 20 us or more; per XCD: clock / per-tile time / last end")
+    print(f"kernel: {kernel}")
+    print(f"workload: {workload_name}")
+    print(f"event_ms: {ms:.4f}")
+    print("\n".join(timeline_summary(recs, 256 * workgroups_per_cu)))
+
+
 def algorithmic_bytes(w):
     """Q, K, V read once and O written once (fp8: 1-byte inputs, bf16 output),
     plus the per-(sequence, head) scales of the fp8 path. Q and O hold the
@@ -410,6 +526,10 @@ def main():
     import packed_varlen_masked_attn_amd as pva
 
     assert torch.cuda.is_available(), "bench.py needs a ROCm GPU"
+    if args.timeline:
+        if args.split_keys > 1:
+            sys.exit("--timeline records single launches (no --split-keys)")
+        pva.use_timeline_build()
     if args.copy_calibration:
         copy_calibration()
         return
@@ -497,6 +617,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    if args.timeline:
+        timeline_run(desc, step, dtype, args.workload, w.name, 2 if is_fp8 else 3)
+        return
 
     # ---------------- timed region: exactly K steps, HIP events per launch on the launch stream
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]

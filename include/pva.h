@@ -391,6 +391,38 @@ int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
 int pva_merge_partials(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows,
                        int32_t head_dim, void* out, float* lse_out, void* stream);
 
+/*
+ * Workgroup timeline, for performance analysis (timing build only).
+ * libpva_timeline.so is this library compiled with PVA_WG_TIMELINE: the same
+ * calls and kernels, except that each launch of a forward kernel also writes
+ * one record per work item (workgroup) into a fixed per-device buffer of that
+ * kernel, PVA_TIMELINE_FIELDS uint64 per record, at the item's index in the
+ * work list:
+ *   [0] real-time counter (100 MHz) when the workgroup starts
+ *   [1] the same after its prologue (work item, key limits, Q and the first
+ *       K/V tiles in place)
+ *   [2] the same after its tile loop (the first wave's last key tile)
+ *   [3] the same at its end (output stored)
+ *   [4] [5] shader-clock counter after the prologue and after the loop
+ *   [6] HW_ID of the wave (CU in bits 11:8, shader array bit 12, engine
+ *       bits 15:13), [7] XCC_ID (XCD in bits 3:0)
+ *   [8] key tiles the first wave computes, [9] key tiles of the item
+ *   [10] workgroup index, [11] 1 once written (empty work-list slots write
+ *       nothing)
+ *   kernel : PVA_BF16 (the contiguous and the paged bf16 kernels share one
+ *            buffer) or PVA_FP8_E4M3
+ * pva_timeline_clear zeroes the kernel's records on the current device;
+ * pva_timeline_read copies records [0, n_records) to host memory
+ * (n_records <= PVA_TIMELINE_MAX_ITEMS). Both synchronise the device. A
+ * launch overwrites the records of its own work items only, so clear before
+ * the launch to be read. The library's own build returns
+ * PVA_ERR_UNSUPPORTED from both.
+ */
+#define PVA_TIMELINE_FIELDS 12
+#define PVA_TIMELINE_MAX_ITEMS 131072
+int pva_timeline_clear(pva_dtype kernel);
+int pva_timeline_read(pva_dtype kernel, uint64_t* host_records, int64_t n_records);
+
 /* Thread-local message of the last failing call on this thread ("" if none). */
 const char* pva_last_error(void);
 

@@ -16,6 +16,11 @@ import numpy as np
 _PKG = os.path.dirname(os.path.abspath(__file__))
 # the in-tree build (python -m packed_varlen_masked_attn_amd.build)
 LIB_PATH = os.path.join(_PKG, "libpva.so")
+# the same build with the per-workgroup timeline compiled in (performance
+# analysis only; selected with use_timeline_build())
+LIB_TIMELINE_PATH = os.path.join(_PKG, "libpva_timeline.so")
+TIMELINE_FIELDS = 12        # PVA_TIMELINE_FIELDS
+TIMELINE_MAX_ITEMS = 131072  # PVA_TIMELINE_MAX_ITEMS
 
 PVA_OK = 0
 PVA_ERR_INVALID_ARG = -1
@@ -34,7 +39,7 @@ EXPORTED = [
     "packed_attn_fwd_varlen_fp8", "pva_last_error", "pva_version", "pva_seg_desc_build_kv_chunk",
     "pva_seg_desc_build_kv_chunk_host", "packed_attn_fwd_partial", "pva_merge_partials", "packed_attn_fwd_paged",
     "packed_attn_fwd_partial_fp8", "pva_seg_desc_build_noalloc", "packed_attn_fwd_partial_accumulate",
-    "packed_attn_fwd_partial_accumulate_fp8",
+    "packed_attn_fwd_partial_accumulate_fp8", "pva_timeline_clear", "pva_timeline_read",
 ]
 
 
@@ -55,6 +60,15 @@ def lib() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m packed_varlen_masked_attn_amd.build` (there is no fallback path)")
+    # PyTorch for ROCm carries its own HIP runtime (libamdhip64.so.7). Loaded
+    # after torch, the library binds to that same runtime, so torch's device
+    # pointers and streams are valid in its calls. Loaded first, it would pull
+    # in the system runtime and torch would then start a second one, which
+    # finds no device.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     L = ctypes.CDLL(LIB_PATH)
 
     def sig(name, argtypes, restype):
@@ -97,10 +111,48 @@ def lib() -> ctypes.CDLL:
     sig("packed_attn_fwd_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
     sig("packed_attn_fwd_varlen", [vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
     sig("packed_attn_fwd_varlen_fp8", [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_float, vp, vp], ctypes.c_int)
+    sig("pva_timeline_clear", [ctypes.c_int], ctypes.c_int)
+    sig("pva_timeline_read", [ctypes.c_int, ctypes.POINTER(ctypes.c_uint64), ctypes.c_int64], ctypes.c_int)
     sig("pva_last_error", [], ctypes.c_char_p)
     sig("pva_version", [], ctypes.c_char_p)
     _lib_handle = L
     return L
+
+
+def use_timeline_build() -> None:
+    """Make this process load libpva_timeline.so instead of libpva.so: the
+    same calls and kernels, which also record a per-workgroup timeline
+    (timeline_clear / timeline_read). Call it before anything has loaded the
+    library."""
+    global LIB_PATH
+    if _lib_handle is not None and LIB_PATH != LIB_TIMELINE_PATH:
+        raise RuntimeError("the library is already loaded; select the timeline build first")
+    LIB_PATH = LIB_TIMELINE_PATH
+
+
+def timeline_clear(kernel: str = "bf16") -> None:
+    """Zero the workgroup-timeline records of the bf16 or fp8 kernels on the
+    current device (timeline build only; synchronises the device)."""
+    if kernel not in DTYPES:
+        raise PvaError(PVA_ERR_INVALID_ARG, f"kernel must be one of {sorted(DTYPES)}")
+    _check(lib().pva_timeline_clear(DTYPES[kernel]))
+
+
+def timeline_read(kernel: str, n_items: int) -> np.ndarray:
+    """uint64 [n_items, TIMELINE_FIELDS] records of work items 0..n_items-1
+    of the last launches of that kernel (timeline build only): real-time
+    counter (100 MHz) at start, after the prologue, after the tile loop and
+    at the end; shader-clock counter after the prologue and after the loop;
+    HW_ID, XCC_ID; key tiles of the first wave and of the item; workgroup
+    index; 1 if written."""
+    if kernel not in DTYPES:
+        raise PvaError(PVA_ERR_INVALID_ARG, f"kernel must be one of {sorted(DTYPES)}")
+    if not 0 <= n_items <= TIMELINE_MAX_ITEMS:
+        raise PvaError(PVA_ERR_INVALID_ARG, f"n_items must lie in [0, {TIMELINE_MAX_ITEMS}]")
+    out = np.zeros((n_items, TIMELINE_FIELDS), dtype=np.uint64)
+    _check(lib().pva_timeline_read(DTYPES[kernel], out.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)),
+                                   int(n_items)))
+    return out
 
 
 def _check(status: int) -> None:

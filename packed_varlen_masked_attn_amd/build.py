@@ -1,4 +1,6 @@
-"""Build libpva.so (HIP kernels for gfx950 + host planner + C-ABI) in-tree.
+"""Build libpva.so (HIP kernels for gfx950 + host planner + C-ABI) in-tree,
+and libpva_timeline.so, the same sources with the per-workgroup timeline
+compiled in (PVA_WG_TIMELINE; for performance analysis only).
 
 Usage: python -m packed_varlen_masked_attn_amd.build [-v]
 """
@@ -15,6 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpva.so")
+BUILD_TIMELINE = os.path.join(ROOT, "_build", "timeline")
+LIB_TIMELINE = os.path.join(PKG, "libpva_timeline.so")
 
 SOURCES = ["plan.cpp", "api.cpp", "fwd_bf16.hip", "fwd_fp8.hip", "merge.hip", "noalloc.hip"]
 ARCH = "gfx950"
@@ -33,13 +37,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libpva.so")
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _compile(src: str, verbose: bool, timeline: bool = False) -> str:
     path = os.path.join(CSRC, src)
-    obj = os.path.join(BUILD, src + ".o")
+    obj = os.path.join(BUILD_TIMELINE if timeline else BUILD, src + ".o")
+    extra = ["-DPVA_WG_TIMELINE"] if timeline else []
     if src.endswith(".hip"):
-        cmd = [hipcc(), "-x", "hip", *COMMON, *DEVICE, "-c", path, "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *COMMON, *extra, *DEVICE, "-c", path, "-o", obj]
     else:
-        cmd = [hipcc(), *COMMON, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
+        cmd = [hipcc(), *COMMON, *extra, "-D__HIP_PLATFORM_AMD__", "-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,19 +56,31 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libpva.so next to this file. Always rebuilds."""
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> str:
+    tmp = lib + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
-        raise RuntimeError(f"linking libpva.so failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+        raise RuntimeError(f"linking {os.path.basename(lib)} failed:\n{res.stdout}\n{res.stderr}")
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, timeline: bool = True) -> str:
+    """Compile every source and link libpva.so next to this file (and, with
+    `timeline`, libpva_timeline.so). Always rebuilds. Returns libpva.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES]
+    if timeline:
+        os.makedirs(BUILD_TIMELINE, exist_ok=True)
+        jobs += [(s, True) for s in SOURCES]
+    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    if timeline:
+        _link(objs[len(SOURCES):], LIB_TIMELINE, verbose)
     return LIB
 
 

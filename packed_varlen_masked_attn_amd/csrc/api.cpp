@@ -455,8 +455,46 @@ int packed_attn_fwd_partial_accumulate_fp8(const void* q, const void* k, const v
   return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, spec, stream);
 }
 
+int pva_timeline_clear(pva_dtype kernel) {
+  if (kernel != PVA_BF16 && kernel != PVA_FP8_E4M3) return set_error(PVA_ERR_INVALID_ARG, "unknown kernel dtype");
+  void* p = nullptr;
+  const int st = kernel == PVA_BF16 ? pva::timeline_records_bf16(&p) : pva::timeline_records_fp8(&p);
+  if (st == PVA_ERR_UNSUPPORTED)
+    return set_error(st, "this build records no workgroup timeline (libpva_timeline.so does)");
+  if (st != PVA_OK) return set_error(st, "locating the timeline records failed");
+  const size_t bytes = size_t(PVA_TIMELINE_MAX_ITEMS) * PVA_TIMELINE_FIELDS * sizeof(uint64_t);
+  hipError_t e = hipMemset(p, 0, bytes);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_error(e, "clearing the timeline records");
+  return ok();
+}
+
+int pva_timeline_read(pva_dtype kernel, uint64_t* host_records, int64_t n_records) {
+  if (kernel != PVA_BF16 && kernel != PVA_FP8_E4M3) return set_error(PVA_ERR_INVALID_ARG, "unknown kernel dtype");
+  if (!host_records) return set_error(PVA_ERR_INVALID_ARG, "host_records is NULL");
+  if (n_records < 0 || n_records > PVA_TIMELINE_MAX_ITEMS)
+    return set_error(PVA_ERR_INVALID_ARG, "n_records must lie in [0, PVA_TIMELINE_MAX_ITEMS]");
+  void* p = nullptr;
+  const int st = kernel == PVA_BF16 ? pva::timeline_records_bf16(&p) : pva::timeline_records_fp8(&p);
+  if (st == PVA_ERR_UNSUPPORTED)
+    return set_error(st, "this build records no workgroup timeline (libpva_timeline.so does)");
+  if (st != PVA_OK) return set_error(st, "locating the timeline records failed");
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess && n_records > 0)
+    e = hipMemcpy(host_records, p, size_t(n_records) * PVA_TIMELINE_FIELDS * sizeof(uint64_t),
+                  hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_error(e, "reading the timeline records");
+  return ok();
+}
+
 const char* pva_last_error(void) { return g_last_error.c_str(); }
 
-const char* pva_version(void) { return "pva 0.3 gfx950"; }
+const char* pva_version(void) {
+#ifdef PVA_WG_TIMELINE
+  return "pva 0.3 gfx950 (workgroup timeline)";
+#else
+  return "pva 0.3 gfx950";
+#endif
+}
 
 }  // extern "C"

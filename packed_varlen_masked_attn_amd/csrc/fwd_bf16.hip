@@ -44,6 +44,13 @@ namespace pva {
 
 namespace {
 
+#ifdef PVA_WG_TIMELINE
+__device__ unsigned long long g_timeline[uint64_t(PVA_TIMELINE_MAX_ITEMS) * PVA_TIMELINE_FIELDS];
+__device__ __forceinline__ unsigned long long* timeline_records() { return g_timeline; }
+#else
+__device__ __forceinline__ unsigned long long* timeline_records() { return nullptr; }
+#endif
+
 template <int D>
 struct Bf16Cfg {
   static constexpr int BM = kBf16BlockM, BN = kBf16BlockN, NW = BM / 32, NT = 64 * NW;
@@ -277,6 +284,8 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   uint8_t* const kst[NS] = {k0s, k1s, k2s};
   uint8_t* const vst[NS] = {v0s, v1s, v2s};
 
+  WgTimeline tl;
+  tl.start();
   const WorkItem it = items[blockIdx.x];
   if (it.seq < 0) return;  // empty slot; uniform over the workgroup
 
@@ -401,6 +410,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   // K0, K1, V0 must have landed; K2 V1 may still be in flight
   wait_vmcnt<Cfg::DMA_MIN>();
   lds_barrier();
+  tl.prologue_done();
 
   f32x16 sa, sb;
   // S(0) and its reference max. Rows past the sequence end, and tiles past a
@@ -473,6 +483,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
     if (j + 5 >= wkend) break;
     iteration(I2{}, j + 5, sb, sa);
   }
+  tl.loop_done();
   // the rest of the item's tiles: the same barriers and DMA as an iteration
   // above, none of its arithmetic
   for (int j = wkend; j < kend; ++j) {
@@ -502,6 +513,7 @@ __device__ __forceinline__ void fwd_bf16_body(const __bf16* __restrict__ Q,
   if (qrow < qend)
     write_row<NDB>(out, qbase + int64_t(qrow) * rs, int64_t(it.qo_row - it.q0 + qrow) * H + it.head, g, oacc, inv,
                    lt > 0.0f ? 0.6931471805599453f * (st.m + __log2f(lt)) : -INFINITY);
+  tl.finish(timeline_records(), wkend, kend);
 }
 
 // Two kernels over the same body: K/V contiguous in [N, H, D], or paged.
@@ -546,6 +558,15 @@ int launch(const void* q, const void* k, const void* v, const int32_t* cu, const
 }
 
 }  // namespace
+
+int timeline_records_bf16(void** ptr) {
+#ifdef PVA_WG_TIMELINE
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(g_timeline)) == hipSuccess ? PVA_OK : PVA_ERR_HIP;
+#else
+  (void)ptr;
+  return PVA_ERR_UNSUPPORTED;
+#endif
+}
 
 int launch_fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu, const pva_seg_desc* d,
                     float scale, const OutSpec& out, const PagedKV* paged, hipStream_t stream) {

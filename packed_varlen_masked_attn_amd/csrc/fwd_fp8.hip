@@ -42,6 +42,13 @@ namespace pva {
 
 namespace {
 
+#ifdef PVA_WG_TIMELINE
+__device__ unsigned long long g_timeline[uint64_t(PVA_TIMELINE_MAX_ITEMS) * PVA_TIMELINE_FIELDS];
+__device__ __forceinline__ unsigned long long* timeline_records() { return g_timeline; }
+#else
+__device__ __forceinline__ unsigned long long* timeline_records() { return nullptr; }
+#endif
+
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // Probabilities are quantised to E4M3 as p = 2^(score - m + kP8Shift), m the
@@ -310,6 +317,8 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   uint8_t* const kst[NS] = {k0s, k1s, k2s, k3s};
   uint8_t* const vst[NS] = {v0s, v1s, v2s, v3s};
 
+  WgTimeline tl;
+  tl.start();
   const WorkItem it = items[blockIdx.x];
   if (it.seq < 0) return;  // empty slot; uniform over the workgroup
 
@@ -433,6 +442,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
 
   wait_vmcnt<2 * Cfg::DMA_MIN>();
   lds_barrier();
+  tl.prologue_done();
 
   auto s_mfma = [&](f32x16(&s)[NB], const uint8_t* kt) {
 #pragma unroll
@@ -508,6 +518,7 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     if (j + 3 >= wkend) break;
     iteration(I3{}, j + 3, sb, sa);
   }
+  tl.loop_done();
   // the rest of the item's tiles: the same barriers and DMA as an iteration
   // above, none of its arithmetic
   for (int j = wkend; j < kend; ++j) {
@@ -532,9 +543,19 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
     write_row<NDB>(out, qbase + int64_t(qrow) * rs, int64_t(it.qo_row - it.q0 + qrow) * H + it.head, g, oacc,
                    lt > 0.0f ? vs / lt : 0.0f, lt > 0.0f ? 0.6931471805599453f * (mb + __log2f(lt)) : -INFINITY);
   }
+  tl.finish(timeline_records(), wkend, kend);
 }
 
 }  // namespace
+
+int timeline_records_fp8(void** ptr) {
+#ifdef PVA_WG_TIMELINE
+  return hipGetSymbolAddress(ptr, HIP_SYMBOL(g_timeline)) == hipSuccess ? PVA_OK : PVA_ERR_HIP;
+#else
+  (void)ptr;
+  return PVA_ERR_UNSUPPORTED;
+#endif
+}
 
 int launch_fwd_fp8(const void* q, const void* k, const void* v, const float* qs, const float* ks, const float* vs,
                    const int32_t* cu, const pva_seg_desc* d, float scale, const OutSpec& out, hipStream_t stream) {

@@ -48,6 +48,56 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Workgroup timeline of the timing build (the library compiled with
+// PVA_WG_TIMELINE, libpva_timeline.so). Thread 0 of each work item's
+// workgroup keeps the real-time counter (100 MHz) at the workgroup's start,
+// after its prologue, after its tile loop and at its end, the shader-clock
+// counter after the prologue and after the loop, and stores them with the
+// hardware ids of its CU and XCD into record blockIdx.x of its kernel's
+// buffer (layout in include/pva.h, pva_timeline_read). In the library's own
+// build the struct is empty and every call compiles to nothing.
+struct WgTimeline {
+#ifdef PVA_WG_TIMELINE
+  uint64_t t0 = 0, t1 = 0, t2 = 0, c1 = 0, c2 = 0;
+  __device__ __forceinline__ void start() { t0 = __builtin_amdgcn_s_memrealtime(); }
+  __device__ __forceinline__ void prologue_done() {
+    t1 = __builtin_amdgcn_s_memrealtime();
+    c1 = __builtin_amdgcn_s_memtime();
+  }
+  __device__ __forceinline__ void loop_done() {
+    t2 = __builtin_amdgcn_s_memrealtime();
+    c2 = __builtin_amdgcn_s_memtime();
+  }
+  // `buf`: the kernel's record array; `tiles`: the first wave's key tiles;
+  // `kend`: the item's key tiles
+  __device__ __forceinline__ void finish(unsigned long long* buf, int tiles, int kend) const {
+    const uint64_t t3 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x != 0 || blockIdx.x >= PVA_TIMELINE_MAX_ITEMS) return;
+    uint32_t hw, xcc;
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_HW_ID)" : "=s"(hw));
+    asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+    unsigned long long* r = buf + uint64_t(PVA_TIMELINE_FIELDS) * blockIdx.x;
+    r[0] = t0;
+    r[1] = t1;
+    r[2] = t2;
+    r[3] = t3;
+    r[4] = c1;
+    r[5] = c2;
+    r[6] = hw;
+    r[7] = xcc;
+    r[8] = uint64_t(tiles);
+    r[9] = uint64_t(kend);
+    r[10] = blockIdx.x;
+    r[11] = 1;  // record written
+  }
+#else
+  __device__ __forceinline__ void start() {}
+  __device__ __forceinline__ void prologue_done() {}
+  __device__ __forceinline__ void loop_done() {}
+  __device__ __forceinline__ void finish(unsigned long long*, int, int) const {}
+#endif
+};
+
 // Workgroup barrier without the global-memory fence __syncthreads() implies
 // (that fence would also wait for every DMA still in flight). LDS reads issued
 // before it have been consumed by then; the memory clobber keeps the

@@ -129,6 +129,11 @@ constexpr size_t kNoAllocScratchBytes = PVA_NOALLOC_SCRATCH_BYTES;
 int scratch_acquire(int device, size_t bytes, void** ptr, uint64_t* generation, std::string* err);
 bool scratch_is_current(int device, uint64_t generation);
 
+// Device address of a forward kernel's workgroup-timeline records on the
+// current device (the timing build only; PVA_ERR_UNSUPPORTED otherwise).
+int timeline_records_bf16(void** ptr);
+int timeline_records_fp8(void** ptr);
+
 // Validates and plans; on failure returns a status and fills `err`.
 // Two segments per sequence: text (causal) then one image block (full).
 int build_plan(const int32_t* text_len, const int32_t* image_len, int32_t nseq, int32_t num_heads,

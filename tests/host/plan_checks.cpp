@@ -45,6 +45,9 @@ int scratch_acquire(int, size_t, void**, uint64_t*, std::string*) {
   std::abort();
 }
 bool scratch_is_current(int, uint64_t) { return false; }
+// as in the library's own build, which records no workgroup timeline
+int timeline_records_bf16(void**) { return PVA_ERR_UNSUPPORTED; }
+int timeline_records_fp8(void**) { return PVA_ERR_UNSUPPORTED; }
 }  // namespace pva
 
 namespace {
@@ -389,11 +392,25 @@ void reject_cases() {
 
 }  // namespace
 
+// The workgroup-timeline calls validate their arguments before touching a
+// device, and the library's own build refuses them.
+void timeline_cases() {
+  uint64_t buf[PVA_TIMELINE_FIELDS * 2] = {};
+  expect(pva_timeline_clear(static_cast<pva_dtype>(7)) == PVA_ERR_INVALID_ARG, "timeline: unknown kernel");
+  expect(pva_timeline_read(PVA_BF16, nullptr, 2) == PVA_ERR_INVALID_ARG, "timeline: NULL records");
+  expect(pva_timeline_read(PVA_BF16, buf, -1) == PVA_ERR_INVALID_ARG, "timeline: negative count");
+  expect(pva_timeline_read(PVA_FP8_E4M3, buf, int64_t(PVA_TIMELINE_MAX_ITEMS) + 1) == PVA_ERR_INVALID_ARG,
+         "timeline: count past the buffer");
+  expect(pva_timeline_clear(PVA_BF16) == PVA_ERR_UNSUPPORTED, "timeline: library build refuses clear");
+  expect(pva_timeline_read(PVA_FP8_E4M3, buf, 2) == PVA_ERR_UNSUPPORTED, "timeline: library build refuses read");
+}
+
 int main(int argc, char** argv) {
   const int n_cases = argc > 1 ? std::atoi(argv[1]) : 400;
   check_range_functions();
   two_segment_cases();
   reject_cases();
+  timeline_cases();
   for (uint64_t seed = 1; seed <= 4; ++seed) random_cases(seed, n_cases / 4);
   std::printf("host checks: %ld checks, %d failures\n", g_checks, g_failures);
   return g_failures == 0 ? 0 : 1;

@@ -6,6 +6,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import numpy as np
 import pytest
@@ -250,3 +251,56 @@ def test_paged_rejects_on_host(case):
     assert st == pva.PVA_ERR_INVALID_ARG
     if case == "host_only":
         assert "host-only" in L.pva_last_error().decode()
+
+
+def test_timeline_calls_in_the_library_build():
+    """The library's own build records no workgroup timeline: both calls
+    refuse on the host, with a message naming the timing build."""
+    L = pva.lib()
+    buf = np.zeros((4, binding.TIMELINE_FIELDS), np.uint64)
+    assert L.pva_timeline_clear(0) == pva.PVA_ERR_UNSUPPORTED
+    assert b"libpva_timeline.so" in L.pva_last_error()
+    assert L.pva_timeline_read(1, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_uint64)), 4) == pva.PVA_ERR_UNSUPPORTED
+    assert L.pva_timeline_clear(7) == pva.PVA_ERR_INVALID_ARG
+    assert L.pva_timeline_read(0, None, 4) == pva.PVA_ERR_INVALID_ARG
+    with pytest.raises(pva.PvaError):
+        pva.timeline_clear("bf16")
+
+
+def test_timeline_build_exports_the_same_calls():
+    """libpva_timeline.so (built beside libpva.so) exports every call the
+    header declares and says which build it is; its header constants match
+    the binding's."""
+    assert os.path.exists(binding.LIB_TIMELINE_PATH), "build() also builds libpva_timeline.so"
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_TIMELINE_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for n in header_functions():
+        assert n in exported, n
+    T = ctypes.CDLL(binding.LIB_TIMELINE_PATH)
+    T.pva_version.restype = ctypes.c_char_p
+    assert b"timeline" in T.pva_version() and b"timeline" not in pva.lib().pva_version()
+    text = open(HEADER).read()
+    assert f"#define PVA_TIMELINE_FIELDS {binding.TIMELINE_FIELDS}" in text
+    assert f"#define PVA_TIMELINE_MAX_ITEMS {binding.TIMELINE_MAX_ITEMS}" in text
+
+
+def test_timeline_build_is_selected_before_loading():
+    """Switching to the timing build after the library is loaded is refused."""
+    pva.lib()
+    with pytest.raises(RuntimeError):
+        pva.use_timeline_build()
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """A process that uses the library before importing torch still maps a
+    single HIP runtime (torch's), so torch's devices, pointers and streams
+    stay valid in the library's calls."""
+    code = ("import packed_varlen_masked_attn_amd as pva\n"
+            "d = pva.SegDesc([3, 4], [5, 6], 2, 64, 'bf16', host_only=True)\n"
+            "import torch\n"
+            "print('\\n'.join(sorted(set(l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l))))\n")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    runtimes = [l for l in res.stdout.splitlines() if l.strip()]
+    assert len(runtimes) == 1, runtimes

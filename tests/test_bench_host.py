@@ -1,9 +1,10 @@
-"""Host-side pieces of bench.py: the single-GPU guard and the rocprofv3 counter summaries."""
+"""Host-side pieces of bench.py: the single-GPU guard, the rocprofv3 counter summaries and the workgroup-timeline summary."""
 import csv
 import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -189,3 +190,32 @@ def test_next_row_arguments_parse(monkeypatch):
         a = bench.parse()
         assert a.workload in workloads.WORKLOADS, name
         assert a.kernel_only or a.split_keys > 1, name
+
+
+def test_timeline_summary_of_known_records():
+    """Two CUs, three workgroups each (real-time ticks of 10 ns, a shader
+    clock of 1.5 GHz): the summary's per-tile time, cycles, prologue,
+    epilogue, refill gap, clocks and CU time shares follow from the records."""
+    rows = []
+    # (cu, start, prologue end, loop end, end) in ticks; 10 tiles per item
+    plan = [(0, 0, 300, 10300, 10500), (0, 0, 300, 10300, 10500), (0, 10600, 10900, 20900, 21100),
+            (1, 0, 300, 10300, 10500), (1, 0, 300, 10300, 10500), (1, 10600, 10900, 20900, 21100)]
+    for i, (cu, a, b, c, d) in enumerate(plan):
+        cyc = (c - b) * 10 * 1.5  # ns * GHz
+        rows.append([a, b, c, d, 1000, 1000 + int(cyc), cu << 8, 0, 10, 10, i, 1])
+    rows.append([0] * 12)  # an empty slot (not written)
+    lines = dict(l.split(": ", 1) for l in bench.timeline_summary(np.array(rows, dtype=np.uint64), 6))
+    assert lines["records"] == "6"
+    assert lines["cus"] == "2"
+    assert float(lines["span_us"]) == pytest.approx(211.0)
+    assert float(lines["per_tile_ns_median"]) == pytest.approx(10000.0)
+    assert float(lines["per_tile_shader_cycles_median"]) == pytest.approx(15000.0)
+    assert float(lines["prologue_us_median"]) == pytest.approx(3.0)
+    assert float(lines["epilogue_us_median"]) == pytest.approx(2.0)
+    assert float(lines["refill_gap_us_median"]) == pytest.approx(1.0)
+    assert float(lines["shader_clock_ghz_median"]) == pytest.approx(1.5)
+    shares = dict(kv.split(":") for kv in lines["cu_time_pct_with_k_computing_workgroups"].split())
+    # per CU: two loops over [3, 103) us, one over [109, 209) us, within 211 us
+    assert float(shares["2"]) == pytest.approx(100 * 100 / 211, abs=0.1)
+    assert float(shares["1"]) == pytest.approx(100 * 100 / 211, abs=0.1)
+    assert float(shares["0"]) == pytest.approx(100 * 11 / 211, abs=0.1)
