@@ -685,7 +685,7 @@ def main():
         "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_TFLOPS[dtype], 4),
         "traffic": None if args.paged else stored_traffic(dtype, w.name),
-        "kernel": ("fwd_fp8_kernel<128>" if is_fp8 else f"fwd_bf16_kernel<{D}>") + (" (paged K/V)" if args.paged else ""),
+        "kernel": ("fwd_fp8_kernel" if is_fp8 else f"fwd_bf16_kernel<{D}>") + (" (paged K/V)" if args.paged else ""),
         "algorithmic_bytes": algorithmic_bytes(w),
     }
     if result["roofline"]["traffic"]:
