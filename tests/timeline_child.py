@@ -11,6 +11,7 @@ sys.path.insert(0, os.path.dirname(HERE))
 sys.path.insert(0, HERE)
 
 import numpy as np  # noqa: E402
+import torch  # noqa: E402
 
 import packed_varlen_masked_attn_amd as pva  # noqa: E402
 from gpu_util import run_bf16, run_fp8, say  # noqa: E402
@@ -24,8 +25,8 @@ def main(out_dir):
         pva.timeline_clear(kernel)
         out, *_, desc = run_bf16(w) if kernel == "bf16" else run_fp8(w)
         recs = pva.timeline_read(kernel, len(desc.work_items))
-        np.savez(os.path.join(out_dir, name + ".npz"), out=out.view(dtype=__import__("torch").int16).cpu().numpy(),
-                 records=recs, items=np.asarray(desc.work_items), version=pva.version())
+        np.savez(os.path.join(out_dir, name + ".npz"), out=out.view(torch.int16).cpu().numpy(), records=recs,
+                 items=np.asarray(desc.work_items), version=pva.version())
 
 
 if __name__ == "__main__":
