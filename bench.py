@@ -507,8 +507,8 @@ def copy_calibration():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs the attention on a single MI355X "
-              "(a multi-GPU run would shard heads or sequences, which is not built). Use --gpus 1.",
+        print("bench.py measures one GPU only: the library runs the attention on a single MI355X "
+              "(a multi-GPU run would shard heads or sequences, which is not implemented). Use --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 

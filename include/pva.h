@@ -57,7 +57,7 @@ extern "C" {
 typedef enum {
   PVA_OK = 0,
   PVA_ERR_INVALID_ARG = -1, /* a size, pointer, alignment or value is out of range   */
-  PVA_ERR_UNSUPPORTED = -2, /* a valid request this build does not implement (e.g. D) */
+  PVA_ERR_UNSUPPORTED = -2, /* a valid request the library does not implement (e.g. D) */
   PVA_ERR_HIP = -3,         /* a HIP runtime call or kernel launch failed              */
   PVA_ERR_NO_MEMORY = -4    /* host or device allocation failed                        */
 } pva_status;

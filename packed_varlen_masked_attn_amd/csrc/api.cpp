@@ -195,7 +195,7 @@ int fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, c
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
   st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, s);
-  if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "fp8 path not available in this build");
+  if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "the fp8 kernel takes head_dim 128 and its own tile shape only");
   if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
   return ok();
 }
@@ -460,7 +460,7 @@ int pva_timeline_clear(pva_dtype kernel) {
   void* p = nullptr;
   const int st = kernel == PVA_BF16 ? pva::timeline_records_bf16(&p) : pva::timeline_records_fp8(&p);
   if (st == PVA_ERR_UNSUPPORTED)
-    return set_error(st, "this build records no workgroup timeline (libpva_timeline.so does)");
+    return set_error(st, "this library records no workgroup timeline (libpva_timeline.so does)");
   if (st != PVA_OK) return set_error(st, "locating the timeline records failed");
   const size_t bytes = size_t(PVA_TIMELINE_MAX_ITEMS) * PVA_TIMELINE_FIELDS * sizeof(uint64_t);
   hipError_t e = hipMemset(p, 0, bytes);
@@ -477,7 +477,7 @@ int pva_timeline_read(pva_dtype kernel, uint64_t* host_records, int64_t n_record
   void* p = nullptr;
   const int st = kernel == PVA_BF16 ? pva::timeline_records_bf16(&p) : pva::timeline_records_fp8(&p);
   if (st == PVA_ERR_UNSUPPORTED)
-    return set_error(st, "this build records no workgroup timeline (libpva_timeline.so does)");
+    return set_error(st, "this library records no workgroup timeline (libpva_timeline.so does)");
   if (st != PVA_OK) return set_error(st, "locating the timeline records failed");
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess && n_records > 0)

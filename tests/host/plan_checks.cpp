@@ -23,7 +23,7 @@
 #include "pva.h"
 #include "pva_internal.h"
 
-// This build holds no kernels: the C-ABI layer's launchers are stand-ins
+// This test program holds no kernels: the C-ABI layer's launchers are stand-ins
 // that must never be reached (every call here fails validation on the host).
 namespace pva {
 int launch_fwd_bf16(const void*, const void*, const void*, const int32_t*, const pva_seg_desc*, float, const OutSpec&,
