@@ -260,7 +260,10 @@ int packed_attn_fwd(const void* q, const void* k, const void* v, const int32_t* 
  * FP8 variant: q, k, v are OCP E4M3FN codes [N, H, D] (16-byte aligned) with
  * one fp32 dequantisation scale per (sequence, head) and tensor
  * (q_scale/k_scale/v_scale: device float [nseq * H], index s * H + h), so
- * that the value of a code x is decode(x) * scale. QK^T and PV run on fp8
+ * that the value of a code x is decode(x) * scale. Scales are finite and
+ * >= 0 (they are read on the device, not checked); a zero q or k scale
+ * makes every allowed score of that slice equal, a zero v scale its output
+ * zero. QK^T and PV run on fp8
  * MFMA; the probabilities are quantised to E4M3 for PV; out is bf16
  * [N, H, D]. Otherwise as packed_attn_fwd; the descriptor must have been
  * built with dtype PVA_FP8_E4M3.

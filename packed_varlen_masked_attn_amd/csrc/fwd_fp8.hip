@@ -339,7 +339,10 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(const uint8_t* __restri
   const uint8_t* Kb = K + base;
   const uint8_t* Vb = V + base;
   const int sh = it.seq * H + it.head;
-  const float scale_log2 = q_scale[sh] * k_scale[sh] * scale_log2e;  // log2 units per raw score
+  // log2 units per raw score, kept at least the smallest normal float: a
+  // zero q or k scale (all scores equal) must still turn a masked score
+  // (-inf) into a zero probability, which -inf * 0 would not
+  const float scale_log2 = __builtin_fmaxf(q_scale[sh] * k_scale[sh] * scale_log2e, 1.17549435e-38f);
   const float vs = v_scale[sh];
 
   // this lane's query row and its key limit (rows past the tile: L, the K/V

@@ -177,3 +177,63 @@ def test_fp8_guard_bands_and_determinism():
         outs.append(b[8:8 + N])
     say("[fp8] guard bands, determinism")
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def _running_means(v, w):
+    """Closed form of attention with all scores equal: text row i of a
+    sequence returns the mean of its V rows 0..i, an image row the mean of
+    all L rows of its sequence ([N, H, D] fp64)."""
+    ref = np.empty_like(v)
+    off = oracle.offsets(w.seq_len)
+    for s, (T, L) in enumerate(zip(w.text_len, w.seq_len)):
+        blk = v[off[s]:off[s] + L]
+        csum = np.cumsum(blk, axis=0) / np.arange(1, L + 1)[:, None, None]
+        ref[off[s]:off[s] + L] = csum[L - 1]
+        ref[off[s]:off[s] + T] = csum[:T]
+    return ref
+
+
+def test_fp8_equal_scores_give_running_means():
+    """Closed forms of the fp8 path: with every key code zero, or with
+    q_scale = 0, or with k_scale = 0, every allowed score is equal, so the
+    probabilities are equal E4M3 values and each row returns the mean of the
+    dequantised V rows it may see (text row i: rows 0..i; image row: the
+    whole sequence). Bound: fp32 accumulation and the bf16 output rounding
+    (2^-8 relative), far inside the 6e-2 parity bound."""
+    import torch
+    from oracle import fp8 as ofp8
+    w = workloads.custom([37, 70, 0, 5], [150, 0, 90, 1], 2, 128, seed=7800, dtype="fp8")
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    codes = [x.view(torch.uint8).clone() for x in (q8, k8, v8)]
+    v = ofp8.dequantize(codes[2].numpy(), vs, w.seq_len)
+    ref = _running_means(v, w)
+    zero_k = [codes[0], torch.zeros_like(codes[1]), codes[2]]
+    cases = {
+        "zero key codes": (zero_k, (qs, ks, vs)),
+        "q_scale 0": (codes, (np.zeros_like(qs), ks, vs)),
+        "k_scale 0": (codes, (qs, np.zeros_like(ks), vs)),
+    }
+    for tag, (c, sc) in cases.items():
+        got = f64(_fp8_launch(w, c, sc))
+        err = np.abs(got - ref)
+        say(f"[fp8] equal scores, {tag}: max {err.max():.3e}")
+        assert np.all(err <= np.abs(ref) * 2.0 ** -8 + 1e-4), (tag, float(err.max()))
+
+
+def test_fp8_zero_value_scale_gives_zero_output():
+    """v_scale = 0 for one (sequence, head): that slice's output is exactly
+    zero and every other slice is bitwise what it is with the true scale."""
+    import torch
+    w = workloads.custom([40, 12], [200, 90], 3, 128, seed=7900, dtype="fp8")
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    codes = [x.view(torch.uint8).clone() for x in (q8, k8, v8)]
+    base = _fp8_launch(w, codes, (qs, ks, vs))
+    vs0 = vs.copy()
+    vs0[1, 2] = 0.0
+    out = _fp8_launch(w, codes, (qs, ks, vs0))
+    off = oracle.offsets(w.seq_len)
+    a, b = off[1], off[1] + w.seq_len[1]
+    assert torch.count_nonzero(out[a:b, 2]) == 0
+    mask = torch.ones(out.shape[:2], dtype=torch.bool)
+    mask[a:b, 2] = False
+    assert torch.equal(out[mask], base[mask])
