@@ -126,11 +126,13 @@ def test_partial_lse_score_drift():
     assert lmx <= LSE_MAX_ABS
 
 
-@pytest.mark.parametrize("scale", [1e-3, 0.5, 1.0])
+@pytest.mark.parametrize("scale", [1e-30, 1e-3, 0.5, 1.0, 10.0, 100.0])
 def test_bf16_softmax_scales(scale):
-    """Other softmax scales on N(0,1) inputs: near-uniform weights (1e-3) and
-    peaked ones whose scores spread over tens of log2 units (0.5, 1), where
-    the reference max moves and most probabilities underflow."""
+    """Other softmax scales on N(0,1) inputs: uniform and near-uniform
+    weights (1e-30, 1e-3), peaked ones whose scores spread over tens of log2
+    units (0.5, 1), where the reference max moves and most probabilities
+    underflow, and rows that put all their weight on one key (10, 100:
+    scores spread over thousands of log2 units)."""
     w = workloads.custom([150, 150], [900, 900], 2, 128, seed=5700)
     out, q, k, v, _ = run_bf16(w, scale=scale)
     ref = oracle.packed_attention(f64(q), f64(k), f64(v), w.text_len, w.image_len, scale)
@@ -159,7 +161,19 @@ def _fp8_scale_run(scale, w):
     return mx, mean
 
 
-@pytest.mark.parametrize("scale", [1e-3, 0.2, 0.35, 0.5, 1.0])
+# The E4M3 MFMA does not sum a dot product exactly: a term far below the
+# block's largest product loses its low bits (measured: 448 - 448 + 30 x 2^-6
+# comes out as 0.75, not 0.9375; the bf16 MFMA returns such sums exactly), so
+# a score carries an error of roughly 2^-13 of its largest product. At
+# softmax scale 100 (1,100 times 1/sqrt(128)) that is about a tenth of a
+# log2 unit on the scores of two keys that nearly tie, which moves their
+# weights by a few percent; the 6e-2 bound is then missed on such rows.
+_FP8_SCALE_LIMIT = pytest.mark.xfail(
+    strict=True, reason="E4M3 MFMA accumulation precision: near-tie rows at softmax scale 100 exceed 6e-2")
+
+
+@pytest.mark.parametrize("scale", [1e-30, 1e-3, 0.2, 0.35, 0.5, 1.0, 10.0,
+                                   pytest.param(100.0, marks=_FP8_SCALE_LIMIT)])
 def test_fp8_softmax_scales(scale):
     w = workloads.custom([150, 150], [900, 900], 2, 128, seed=5800, dtype="fp8", name="scales_fp8")
     mx, mean = _fp8_scale_run(scale, w)
