@@ -126,16 +126,19 @@ def test_text_rows_before_a_chunk_have_no_keys():
     assert np.isneginf(lse.cpu().numpy()[:100]).all()
 
 
-@pytest.mark.parametrize("D", [64, 128])
-def test_merge_kernel_alone(D):
+@pytest.mark.parametrize("D,P,rows", [(64, 3, 1000), (128, 3, 1000), (128, 1, 1001), (64, 2, 7), (128, 5, 1003),
+                                      (64, 9, 517)])
+def test_merge_kernel_alone(D, P, rows):
+    """The merge kernel on its own: any number of parts (the kernel reads
+    four at a time), rows that leave a partial last workgroup, parts and rows
+    without keys."""
     import torch
     import packed_varlen_masked_attn_amd as pva
-    rng = np.random.default_rng(2000 + D)
-    P, rows = 3, 1000
+    rng = np.random.default_rng(2000 + D + 10 * P + rows)
     o = rng.standard_normal((P, rows, D)).astype(np.float32)
     l = (3 * rng.standard_normal((P, rows))).astype(np.float32)
-    l[0, :50] = -np.inf            # some parts without keys
-    l[:, 50:60] = -np.inf          # rows without any key
+    l[0, :min(50, rows)] = -np.inf  # some parts without keys
+    l[:, 50:60] = -np.inf           # rows without any key
     ref_o, ref_l = oracle.merge_partials(o.astype(np.float64), l.astype(np.float64))
     out = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
     lo = torch.empty((rows,), dtype=torch.float32, device="cuda")
@@ -143,6 +146,7 @@ def test_merge_kernel_alone(D):
     torch.cuda.synchronize()
     got = f64(out)
     assert np.all(got[50:60] == 0.0) and np.isneginf(lo.cpu().numpy()[50:60]).all()
+    assert np.isfinite(got).all()
     # bf16 output rounding: relative 2^-9 of the largest |O| in a row
     assert np.max(np.abs(got - ref_o)) <= 2.0 ** -8 * max(1.0, float(np.abs(ref_o).max()))
     ok = ~np.isneginf(ref_l)
