@@ -237,3 +237,19 @@ def test_fp8_zero_value_scale_gives_zero_output():
     mask = torch.ones(out.shape[:2], dtype=torch.bool)
     mask[a:b, 2] = False
     assert torch.equal(out[mask], base[mask])
+
+
+def test_fp8_thousands_of_short_sequences():
+    """The fp8 path on 3,000 sequences of 1 to 64 tokens (one short query
+    tile per (sequence, head), per-(sequence, head) scales for each)."""
+    rng = np.random.default_rng(6500)
+    t, i = workloads.random_lengths(rng, 1500, 24, 40)
+    w = workloads.custom(t, i, 2, 128, seed=6600, dtype="fp8", name="short_sequences_fp8")
+    say(f"[fp8] thousands of short sequences: {len(t)} sequences, N={w.total_tokens}")
+    out, q, k, v, _ = run_fp8(w)
+    ref = oracle.packed_attention(q, k, v, w.text_len, w.image_len, 1.0 / math.sqrt(w.head_dim))
+    got = f64(out)
+    mx, mean = err_stats(got, ref)
+    say(f"[fp8] thousands of short sequences: max {mx:.3e} mean {mean:.3e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= FP8_MAX_ABS, (mx, mean)

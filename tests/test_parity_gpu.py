@@ -192,3 +192,21 @@ def test_many_sequences(D):
     t = (1, 1, 0, 0, 127, 127) + t
     i = (0, 0, 1, 1, 129, 129) + i
     _full_compare(workloads.custom(t, i, 2, D, seed=6200 + D), f"many sequences D={D}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_thousands_of_short_sequences(D):
+    """3,000 sequences of 1 to 64 tokens in one pack (1,500 CFG pairs, empty
+    text or image blocks among them): one short query tile per (sequence,
+    head), thousands of work items, most rows of each tile past the end."""
+    rng = np.random.default_rng(6300 + D)
+    t, i = workloads.random_lengths(rng, 1500, 24, 40)
+    w = workloads.custom(t, i, 2, D, seed=6400 + D, name="short_sequences")
+    say(f"[parity] thousands of short sequences: {len(t)} sequences, N={w.total_tokens}, D={D}")
+    out, q, k, v, desc = run_bf16(w)
+    ref = oracle.packed_attention(f64(q), f64(k), f64(v), w.text_len, w.image_len, 1.0 / math.sqrt(D))
+    got = f64(out)
+    mx, mean = err_stats(got, ref)
+    say(f"[parity] thousands of short sequences D={D}: max {mx:.3e} mean {mean:.3e}")
+    assert np.all(np.isfinite(got))
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (mx, mean)
