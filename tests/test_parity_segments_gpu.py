@@ -174,3 +174,34 @@ def _sampled(sw, n_seq_sample=3):
 @pytest.mark.parametrize("name", ["mixed_res_prefix", "edit_segments", "mixed_res_prefix_fp8", "edit_segments_fp8"])
 def test_full_size_sampled(name):
     _sampled(workloads.WORKLOADS[name]())
+
+
+@pytest.mark.parametrize("name", ["edit_segments", "edit_segments_fp8", "mixed_res_prefix"])
+def test_whole_slices(name):
+    """Every queried row of one head of every sequence, at the full sizes of
+    the interleaved-segment and prefix-KV workloads, element by element
+    against the oracle (rows in blocks of 2,048 to bound its score matrix)."""
+    sw = workloads.WORKLOADS[name]()
+    say(f"[segments] whole slices {sw.name}: Nk={sw.total_tokens} Nq={sw.total_q} H={sw.num_heads} {sw.dtype}")
+    out, q, k, v, _ = run_seg(sw)
+    oseqs = _oseqs(sw)
+    qoff = oracle.offsets(sw.q_rows)
+    scale = 1.0 / math.sqrt(sw.head_dim)
+    worst, total, count = 0.0, 0.0, 0
+    for si, s in enumerate(oseqs):
+        h = (5 * si + 1) % sw.num_heads
+        got_all = out[qoff[si]:qoff[si + 1], h].float().cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got_all))
+        for r0 in range(s.q_start, s.length, 2048):
+            rows = list(range(r0, min(s.length, r0 + 2048)))
+            ref = oracle.segment_attention_rows(q, k, v, oseqs, scale, si, rows, [h])[:, 0]
+            d = np.abs(got_all[r0 - s.q_start:r0 - s.q_start + len(rows)] - ref)
+            worst = max(worst, float(d.max()))
+            total += float(d.sum())
+            count += d.size
+    mean = total / count
+    say(f"[segments] whole slices {sw.name}: max {worst:.3e} mean {mean:.3e} over {count} elements")
+    if sw.dtype == "fp8":
+        assert worst <= FP8_MAX_ABS, worst
+    else:
+        assert worst <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (worst, mean)
