@@ -98,3 +98,16 @@ def test_paged_prefix_mixed_batch_full_size():
     out, ref, *_ = _run_both(sw, 256, 11)
     say(f"[paged] mixed batch prefix KV: equal={torch.equal(out, ref)}")
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("block_size", [64, 256])
+def test_paged_full_size_equals_contiguous(block_size):
+    """The prefix-KV mixed batch (the paged row's workload in the bench) with
+    K/V scattered over a NaN-filled pool in random block order: bitwise the
+    contiguous result."""
+    import torch
+    sw = workloads.WORKLOADS["mixed_res_prefix"]()
+    say(f"[paged] full size {sw.name}, blocks of {block_size}")
+    out, ref, *_ = _run_both(sw, block_size, 11 + block_size)
+    assert not torch.isnan(out).any()
+    assert torch.equal(out, ref)
