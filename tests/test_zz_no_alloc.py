@@ -5,7 +5,8 @@ give the same output as with pva_seg_desc_build's descriptor (bitwise: same
 plan, same kernels) and match the oracle at the bf16 tolerances. Two
 no-alloc builds in a row, the second for a smaller batch, reuse one buffer;
 the first descriptor is then refused on the host. A batch whose work list
-exceeds the buffer is refused before any copy."""
+exceeds the buffer is refused before any copy. An fp8 descriptor in the
+buffer serves the fp8 forward like an allocated one."""
 import math
 
 import numpy as np
@@ -120,3 +121,26 @@ def test_noalloc_descriptor_under_graph_capture():
         assert torch.equal(out, want), f"replay {i} differs from the eager launch"
         torch.randn(1 << 20, device="cuda").sum().item()
     say("[noalloc] graph: 4 replays equal to eager")
+
+
+def test_noalloc_fp8_descriptor():
+    """An fp8 descriptor in the fixed buffer: the fp8 forward gives bitwise the
+    output it gives with the allocating builder's descriptor."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    dev = torch.device("cuda:0")
+    w = workloads.custom([150, 150, 40], [900, 900, 300], 4, 128, seed=7310, dtype="fp8", name="noalloc_fp8")
+    say(f"[noalloc] {w.name}: T={w.text_len} I={w.image_len} H={w.num_heads}")
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    q, k, v = (x.view(torch.uint8).to(dev) for x in (q8, k8, v8))
+    sc = [torch.from_numpy(x).to(dev) for x in (qs, ks, vs)]
+    outs = []
+    for noalloc in (True, False):
+        desc = pva.SegDesc(w.text_len, w.image_len, w.num_heads, w.head_dim, "fp8", noalloc=noalloc)
+        cu = torch.from_numpy(desc.cu_seqlens).to(dev)
+        out = torch.empty((w.total_tokens, w.num_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+        pva.packed_attn_fwd_fp8(q, k, v, *sc, cu, desc, 1.0 / math.sqrt(w.head_dim), out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+    assert not torch.isnan(outs[0].float()).any()
