@@ -4,7 +4,8 @@ fp64 oracle, through the C-ABI: random multi-segment packs with suffix
 queries cut into three key chunks (some empty, the first among them), the
 running O starting as NaN (a row the running result has not reached must not
 read it), the chunk-by-chunk intermediate results, equality with partials +
-merge, the full-size mixed batch split in two, and argument errors."""
+merge, the full-size mixed batch split in two (bf16) and in four (fp8), and
+argument errors."""
 import math
 
 import numpy as np
@@ -261,3 +262,57 @@ def test_accumulate_guard_bands():
     mx, mean = err_stats(f64(out), full)
     say(f"[accumulate] guard bands: max {mx:.3e}")
     assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS
+
+
+def test_fp8_accumulate_full_size_four_chunks_sampled():
+    """The fp8 mixed batch with every sequence's keys cut into four equal
+    chunks (the ring of four ranks' key shares): a partial launch and three
+    accumulating ones, the last into the bf16 output, on sampled rows around
+    the chunk edges."""
+    import torch
+    import packed_varlen_masked_attn_amd as pva
+    import workloads
+    from gpu_util import sample_rows
+    from oracle import fp8 as ofp8
+    w = workloads.mixed_res_fp8()
+    seqs = [oracle.make_seq([t, i], [oracle.CAUSAL, oracle.FULL]) for t, i in zip(w.text_len, w.image_len)]
+    q8, k8, v8, qs, ks, vs = workloads.fp8_inputs(w)
+    codes = [x.view(torch.uint8) for x in (q8, k8, v8)]
+    sc = [torch.from_numpy(x).to("cuda") for x in (qs, ks, vs)]
+    H, D = w.num_heads, w.head_dim
+    scale = 1 / math.sqrt(D)
+    cuts = [[s.length * p // 4 for p in range(5)] for s in seqs]
+    o_acc = torch.full((w.total_tokens, H, D), float("nan"), dtype=torch.float32, device="cuda")
+    lse_acc = torch.full((w.total_tokens, H), -float("inf"), dtype=torch.float32, device="cuda")
+    out = torch.empty((w.total_tokens, H, D), dtype=torch.bfloat16, device="cuda")
+    q = codes[0].to("cuda")
+    for p in range(4):
+        lo = [c[p] for c in cuts]
+        hi = [c[p + 1] for c in cuts]
+        desc = _desc(seqs, H, D, lo, hi, "fp8")
+        k = _chunk_rows(codes[1], seqs, lo, hi).to("cuda")
+        v = _chunk_rows(codes[2], seqs, lo, hi).to("cuda")
+        cuq = torch.from_numpy(desc.cu_seqlens_q).to("cuda")
+        cuk = torch.from_numpy(desc.cu_seqlens).to("cuda")
+        if p == 0:
+            pva.packed_attn_fwd_partial_fp8(q, k, v, *sc, cuq, cuk, desc, scale, o_acc, lse_acc)
+        else:
+            pva.packed_attn_fwd_partial_accumulate_fp8(q, k, v, *sc, cuq, cuk, desc, scale, o_acc, lse_acc,
+                                                       out if p == 3 else None)
+    torch.cuda.synchronize()
+    outn = f64(out)
+    assert np.all(np.isfinite(outn))
+    qn = ofp8.dequantize(codes[0].numpy(), qs, w.seq_len)
+    kn = ofp8.dequantize(codes[1].numpy(), ks, w.seq_len)
+    vn = ofp8.dequantize(codes[2].numpy(), vs, w.seq_len)
+    rng = np.random.default_rng(9)
+    off = oracle.offsets(w.seq_len)
+    for si in (1, 4, 7):
+        edges = [c for c in cuts[si][1:4]] + [c - 1 for c in cuts[si][1:4]]
+        rows = sorted(set(r for r in sample_rows(w.text_len[si], w.seq_len[si], rng) + edges
+                          if 0 <= r < w.seq_len[si]))
+        heads = [0, 13, 31]
+        ref = oracle.packed_attention_rows(qn, kn, vn, w.text_len, w.image_len, scale, si, rows, heads)
+        mx, mean = err_stats(outn[off[si] + np.asarray(rows)][:, heads], ref)
+        say(f"[accumulate] fp8 full size, four chunks, seq {si}: max {mx:.3e} mean {mean:.3e}")
+        assert mx <= FP8_MAX_ABS, (si, mx)
