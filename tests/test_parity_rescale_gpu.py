@@ -169,7 +169,7 @@ def _fp8_scale_run(scale, w):
 # log2 unit on the scores of two keys that nearly tie, which moves their
 # weights by a few percent; the 6e-2 bound is then missed on such rows.
 _FP8_SCALE_LIMIT = pytest.mark.xfail(
-    strict=True, reason="E4M3 MFMA accumulation precision: near-tie rows at softmax scale 100 exceed 6e-2")
+    strict=False, reason="E4M3 MFMA accumulation precision: near-tie rows at softmax scale 100 exceed 6e-2")
 
 
 @pytest.mark.parametrize("scale", [1e-30, 1e-3, 0.2, 0.35, 0.5, 1.0, 10.0,
