@@ -284,6 +284,10 @@ int packed_attn_fwd_fp8(const void* q, const void* k, const void* v, const float
  * are device int32 [nseq + 1] equal to the descriptor's (checked with
  * PVA_CHECK=1). Every queried row is written; nothing else in out is
  * touched. Otherwise as packed_attn_fwd.
+ * Tensors of zero rows may be passed as NULL, in this and every other
+ * forward call: q and out (with out_f32, lse, o_acc and lse_acc) when the
+ * descriptor queries no row (every q_start = L: the call checks its
+ * arguments and launches nothing), k and v when its key chunks hold no rows.
  */
 int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                            const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, void* out,
@@ -391,7 +395,8 @@ int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
  *   o_parts   : device float [n_parts, rows, head_dim], 16-byte aligned
  *               (part c's O from packed_attn_fwd_partial is one [rows, D] slab)
  *   lse_parts : device float [n_parts, rows], 4-byte aligned
- *   n_parts   : >= 1; rows >= 0; head_dim in {64, 128}
+ *   n_parts   : >= 1; rows >= 0 (with rows = 0 the pointers may be NULL);
+ *               head_dim in {64, 128}
  *   out       : device bf16 [rows, head_dim], 16-byte aligned
  *   lse_out   : device float [rows], or NULL
  * Asynchronous on `stream`; allocates nothing.

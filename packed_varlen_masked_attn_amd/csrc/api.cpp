@@ -65,7 +65,11 @@ int validate_fwd(const void* q, const void* k, const void* v, const int32_t* cu_
                  const pva_seg_desc* d, float scale, void* out, pva_dtype want) {
   // every check here is host-only and runs before anything touches the device
   if (!d) return set_error(PVA_ERR_INVALID_ARG, "seg_desc is NULL");
-  if (!q || !k || !v || !out || !cu_q || !cu_k) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
+  // a tensor of zero rows may come without an address (q and out when no row
+  // is queried, k and v when the key chunks hold no rows)
+  const bool no_queries = d->plan.total_q == 0, no_keys = d->plan.total_tokens == 0;
+  if (((!q || !out) && !no_queries) || ((!k || !v) && !no_keys) || !cu_q || !cu_k)
+    return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return set_error(PVA_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
   if (!(std::isfinite(scale) && scale > 0.0f)) return set_error(PVA_ERR_INVALID_ARG, "scale must be finite and > 0");
@@ -122,16 +126,19 @@ int build_common(PlanFn plan_fn, Placement placement, void* stream, pva_seg_desc
     d->device = dev;
     const size_t item_bytes = (d->plan.items.size() * sizeof(pva::WorkItem) + 255) / 256 * 256;
     const size_t lim_bytes = d->plan.key_lim.size() * sizeof(int32_t);
+    // never empty: a device descriptor always has a work-list address, also
+    // when it queries no row (then it has no items and no limits)
+    const size_t bytes = std::max<size_t>(item_bytes + lim_bytes, 256);
     void* base = nullptr;
     if (placement == Placement::kScratch) {
       // the fixed buffer is never allocated or freed here
-      st = pva::scratch_acquire(dev, item_bytes + lim_bytes, &base, &d->scratch_generation, &err);
+      st = pva::scratch_acquire(dev, bytes, &base, &d->scratch_generation, &err);
       if (st != PVA_OK) {
         delete d;
         return set_error(st, err);
       }
     } else {
-      e = hipMalloc(&base, item_bytes + lim_bytes);
+      e = hipMalloc(&base, bytes);
       if (e != hipSuccess) {
         delete d;
         return set_error(PVA_ERR_NO_MEMORY, std::string("hipMalloc of the work list: ") + hipGetErrorString(e));
@@ -143,7 +150,8 @@ int build_common(PlanFn plan_fn, Placement placement, void* stream, pva_seg_desc
     if (!d->plan.items.empty())
       e = hipMemcpyAsync(d->d_items, d->plan.items.data(), d->plan.items.size() * sizeof(pva::WorkItem),
                          hipMemcpyHostToDevice, s);
-    if (e == hipSuccess) e = hipMemcpyAsync(d->d_lims, d->plan.key_lim.data(), lim_bytes, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess && lim_bytes > 0)
+      e = hipMemcpyAsync(d->d_lims, d->plan.key_lim.data(), lim_bytes, hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
       if (placement == Placement::kOwnAllocation) (void)hipFree(base);
@@ -181,6 +189,10 @@ int fwd_bf16(const void* q, const void* k, const void* v, const int32_t* cu_q, c
   if (st != PVA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
+  // no key rows: every tile range is empty and nothing is read, but the
+  // kernels still form addresses from a base
+  if (!k) k = d->d_items;
+  if (!v) v = d->d_items;
   st = pva::launch_fwd_bf16(q, k, v, cu_k, d, scale, out, nullptr, s);
   if (st != PVA_OK) return set_error(st, "bf16 kernel launch failed");
   return ok();
@@ -194,6 +206,10 @@ int fwd_fp8(const void* q, const void* k, const void* v, const float* q_scale, c
   if (!q_scale || !k_scale || !v_scale) return set_error(PVA_ERR_INVALID_ARG, "a scale pointer is NULL");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = check_cu(cu_q, cu_k, d, s)) != PVA_OK) return st;
+  // no key rows: every tile range is empty and nothing is read, but the
+  // kernels still form addresses from a base
+  if (!k) k = d->d_items;
+  if (!v) v = d->d_items;
   st = pva::launch_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_k, d, scale, out, s);
   if (st == PVA_ERR_UNSUPPORTED) return set_error(st, "the fp8 kernel takes head_dim 128 and its own tile shape only");
   if (st != PVA_OK) return set_error(st, "fp8 kernel launch failed");
@@ -208,7 +224,7 @@ pva::OutSpec plain_out(void* out) { return pva::OutSpec{out, 0, nullptr, nullptr
 // O goes to out in bf16 (lse_acc is updated either way).
 int accumulate_out(const pva_seg_desc* d, float* o_acc, float* lse_acc, void* out, pva::OutSpec* spec) {
   if (!d) return set_error(PVA_ERR_INVALID_ARG, "seg_desc is NULL");
-  if (!o_acc || !lse_acc) return set_error(PVA_ERR_INVALID_ARG, "o_acc or lse_acc is NULL");
+  if ((!o_acc || !lse_acc) && d->plan.total_q > 0) return set_error(PVA_ERR_INVALID_ARG, "o_acc or lse_acc is NULL");
   if (!aligned16(o_acc)) return set_error(PVA_ERR_INVALID_ARG, "o_acc must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(lse_acc) & 3u) != 0)
     return set_error(PVA_ERR_INVALID_ARG, "lse_acc must be 4-byte aligned");
@@ -350,7 +366,7 @@ int packed_attn_fwd_varlen(const void* q, const void* k, const void* v, const in
 int packed_attn_fwd_partial(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                             const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale, float* out_f32,
                             float* lse, void* stream) {
-  if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
+  if (!lse && !(seg_desc && seg_desc->plan.total_q == 0)) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   return fwd_bf16(q, k, v, cu_seqlens_q, cu_seqlens_k, seg_desc, scale, pva::OutSpec{out_f32, 1, lse, nullptr, nullptr},
                   stream);
@@ -397,9 +413,10 @@ int packed_attn_fwd_paged(const void* q, const void* k_pool, const void* v_pool,
 
 int pva_merge_partials(const float* o_parts, const float* lse_parts, int32_t n_parts, int64_t rows, int32_t head_dim,
                        void* out, float* lse_out, void* stream) {
-  if (!o_parts || !lse_parts || !out) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (n_parts < 1) return set_error(PVA_ERR_INVALID_ARG, "n_parts must be >= 1");
   if (rows < 0) return set_error(PVA_ERR_INVALID_ARG, "rows must be >= 0");
+  // zero rows may come without addresses
+  if ((!o_parts || !lse_parts || !out) && rows > 0) return set_error(PVA_ERR_INVALID_ARG, "a tensor pointer is NULL");
   if (head_dim != 64 && head_dim != 128) return set_error(PVA_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
   if (!aligned16(o_parts) || !aligned16(out)) return set_error(PVA_ERR_INVALID_ARG, "o_parts and out must be 16-byte aligned");
   if ((reinterpret_cast<uintptr_t>(lse_parts) & 3u) != 0 || (reinterpret_cast<uintptr_t>(lse_out) & 3u) != 0)
@@ -430,7 +447,7 @@ int packed_attn_fwd_partial_fp8(const void* q, const void* k, const void* v, con
                                 const float* k_scale, const float* v_scale, const int32_t* cu_seqlens_q,
                                 const int32_t* cu_seqlens_k, const pva_seg_desc* seg_desc, float scale,
                                 float* out_f32, float* lse, void* stream) {
-  if (!lse) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
+  if (!lse && !(seg_desc && seg_desc->plan.total_q == 0)) return set_error(PVA_ERR_INVALID_ARG, "lse is NULL");
   if ((reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return set_error(PVA_ERR_INVALID_ARG, "lse must be 4-byte aligned");
   return fwd_fp8(q, k, v, q_scale, k_scale, v_scale, cu_seqlens_q, cu_seqlens_k, seg_desc, scale,
                  pva::OutSpec{out_f32, 1, lse, nullptr, nullptr}, stream);
