@@ -317,6 +317,8 @@ class SegDesc:
         p = ctypes.POINTER(ctypes.c_int32)()
         n = ctypes.c_int32()
         _check(lib().pva_seg_desc_key_limits(self.handle, ctypes.byref(p), ctypes.byref(n)))
+        if n.value == 0:  # no queried row: the library holds no array
+            return np.zeros(0, np.int32)
         return np.ctypeslib.as_array(p, shape=(n.value,)).copy()
 
     @property

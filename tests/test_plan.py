@@ -283,3 +283,19 @@ def test_kv_chunk_rejects():
             pva.SegDesc.segments(seqs, 2, 64, host_only=True, k_lo=lo, k_hi=hi)
     with pytest.raises(pva.PvaError):
         pva.SegDesc.segments(seqs, 2, 64, host_only=True, k_lo=[0], k_hi=None)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_plan_without_queried_rows(dtype):
+    """Every sequence cached (q_start = L): no queried row, no work item, no
+    key limit and no useful FLOP, while the key side keeps every row."""
+    seqs = [([30, 100], [0, 1], 130), ([5], [1], 5), ([64, 0, 40], [0, 1, 0], 104)]
+    d = pva.SegDesc.segments(seqs, 2, 128, dtype, host_only=True)
+    assert d.total_q == 0 and d.cu_seqlens_q.tolist() == [0, 0, 0, 0]
+    assert d.cu_seqlens.tolist() == [0, 130, 135, 239]
+    assert d.work_items.shape == (0, 8) and d.key_limits.shape == (0,)
+    assert d.useful_flops == 0
+    # one queried row more gives one item per head and that row's limit
+    seqs[1] = ([5], [1], 4)
+    d = pva.SegDesc.segments(seqs, 2, 128, dtype, host_only=True)
+    assert d.total_q == 1 and d.key_limits.tolist() == [5] and len(d.work_items) == 2
