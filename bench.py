@@ -81,6 +81,9 @@ def parse():
                          "others, the last one writing bf16 O) instead of P fp32 partials and a merge")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="time dense library GEMMs (bf16 torch.matmul, E4M3 torch._scaled_mm) at 8192^3 on the "
+                         "same chip, for the MFMA rate that plain dense work reaches under its power limit")
     ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
                     help="summarise rocprofv3 FETCH_SIZE / WRITE_SIZE counter files of --kernel-only runs "
                          "(no GPU needed) and print the traffic record for --workload")
@@ -504,6 +507,47 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
+def gemm_ceiling(steps: int):
+    """Dense library GEMMs on the same chip, for context beside the 2.4 GHz
+    peaks: torch.matmul in bf16 and torch._scaled_mm in E4M3 (per-tensor
+    scales, bf16 out), both at M = N = K = 8192 on N(0,1) data, timed with
+    HIP events on the current stream. Prints one JSON line."""
+    import torch
+    n = 8192
+    flop = 2 * n ** 3
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16, generator=g)
+
+    def timed(fn):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    rec = {"m_n_k": [n, n, n], "steps": steps}
+    ms = timed(lambda: torch.matmul(a, b))
+    tf = flop / ms / 1e9
+    rec["bf16"] = {"op": "torch.matmul", "ms": round(ms, 4), "tflops": round(tf, 1),
+                   "frac_of_peak": round(tf / PEAK_TFLOPS["bf16"], 4)}
+    log(f"[gemm] bf16 {ms:.3f} ms {tf:.1f} TFLOP/s")
+    a8 = a.to(torch.float8_e4m3fn)
+    b8 = b.t().contiguous().to(torch.float8_e4m3fn).t()  # column-major, as _scaled_mm takes its second operand
+    one = torch.ones((), device="cuda", dtype=torch.float32)
+    ms = timed(lambda: torch._scaled_mm(a8, b8, scale_a=one, scale_b=one, out_dtype=torch.bfloat16))
+    tf = flop / ms / 1e9
+    rec["fp8"] = {"op": "torch._scaled_mm e4m3fn", "ms": round(ms, 4), "tflops": round(tf, 1),
+                  "frac_of_peak": round(tf / PEAK_TFLOPS["fp8"], 4)}
+    log(f"[gemm] fp8 {ms:.3f} ms {tf:.1f} TFLOP/s")
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -532,6 +576,9 @@ def main():
         pva.use_timeline_build()
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.gemm_ceiling:
+        gemm_ceiling(args.steps)
         return
     dev = torch.device("cuda:0")
     w = workloads.WORKLOADS[args.workload]()
