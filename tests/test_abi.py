@@ -304,3 +304,23 @@ def test_one_hip_runtime_whatever_the_import_order():
     assert res.returncode == 0, res.stderr[-2000:]
     runtimes = [l for l in res.stdout.splitlines() if l.strip()]
     assert len(runtimes) == 1, runtimes
+
+
+def test_header_is_plain_c(tmp_path):
+    """pva.h is usable from C: a C99 translation unit that includes it and
+    names every declared entry point compiles with -pedantic -Werror."""
+    import shutil
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    header = open(os.path.join(ROOT, "include", "pva.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:int|int64_t|void|const char\*)\s+(\w+)\s*\(", header, re.M)))
+    assert "packed_attn_fwd" in names and "pva_seg_desc_build" in names
+    src = tmp_path / "uses_pva.c"
+    src.write_text('#include "pva.h"\n'
+                   "int main(void) {\n"
+                   + "".join(f"  void (*p{i})(void) = (void (*)(void)){n}; (void)p{i};\n" for i, n in enumerate(names))
+                   + "  return PVA_OK;\n}\n")
+    res = subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I" + os.path.join(ROOT, "include"),
+                          "-fsyntax-only", str(src)], capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
