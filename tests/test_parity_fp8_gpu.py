@@ -42,6 +42,13 @@ FP8_EDGES = {
     "ragged_tail": ([70], [131]),
     "many_short": ([1, 0, 5, 9, 2, 0, 33, 64], [0, 7, 1, 30, 0, 65, 1, 64]),
     "long_text": ([700], [60]),
+    # edges of the fp8 tiles (64 keys, 128 query rows)
+    "single_token_image": ([0], [1]),
+    "text_ends_at_key_tile": ([64], [64]),
+    "text_ends_at_query_tile": ([128], [64]),
+    "text_crosses_query_tile": ([129], [63]),
+    "image_ends_at_key_tile": ([0], [256]),
+    "one_past_key_tile": ([1], [64]),
 }
 
 
