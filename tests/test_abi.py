@@ -324,3 +324,17 @@ def test_header_is_plain_c(tmp_path):
     res = subprocess.run([cc, "-std=c99", "-pedantic", "-Wall", "-Wextra", "-Werror", "-I" + os.path.join(ROOT, "include"),
                           "-fsyntax-only", str(src)], capture_output=True, text=True)
     assert res.returncode == 0, res.stderr
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises (there is no fallback
+    path): the planner, the version query and the forward calls all go
+    through it."""
+    monkeypatch.setattr(binding, "_lib_handle", None)
+    monkeypatch.setattr(binding, "LIB_PATH", str(tmp_path / "libpva.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        pva.SegDesc([4], [12], 2, 64, host_only=True)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.version()
+    with pytest.raises(RuntimeError, match="no fallback"):
+        binding.lib()
